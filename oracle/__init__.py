@@ -1,0 +1,29 @@
+"""CPU oracle for the paged decode path -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 numpy code that states what the GPU path computes, so
+that the GPU path can be checked against it.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it; the library and its Python binding never do, and it shares no code
+with them (the seeded input generator ``paged_kv_cache_198_amd.synth`` is the
+one module both sides read inputs from).
+
+Sources.  The method is described in prose only, on two pages:
+  * "Efficient Memory Management for Large Language Model Serving with
+    PagedAttention" (paper listing), "From the abstract";
+  * "PagedAttention: the KV cache was the bottleneck all along" (blog post),
+    sections "The number that made us read the code" and "Virtual memory for
+    attention".
+The pages give no formula for attention itself; the oracle uses the textbook
+single-query softmax attention, softmax(scale * q . K^T) . V, and the readings
+taken where the pages are silent are listed in each function's docstring.
+
+Pins.  Every function here is checked by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_alloc.py`` against facts fixed by the pages or by
+mathematics (hand-derived fixtures in ``tests/golden/``, closed forms, a dense
+library formula, invariances); none is "parity unpinned".
+
+Modules:
+  decode -- paged single-query decode attention, cache write, block copy,
+            byte accounting;
+  alloc  -- block allocator: free list, reference counts, copy-on-write fork.
+"""

@@ -1,0 +1,127 @@
+"""Oracle: paged KV block allocator with reference counts and copy-on-write.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain Python lists and
+dicts; every rule below is written so that an independent implementation can
+agree with it bit for bit.
+
+What the pages fix ("PagedAttention: the KV cache was the bottleneck all
+along", section "Virtual memory for attention"):
+  * the cache is cut into fixed-size blocks of ``bs`` tokens; a per-sequence
+    block table maps logical blocks to physical ones;
+  * a sequence acquires blocks as it grows (memory is allocated on demand),
+    so only its last block can be partly empty;
+  * completions of one prompt share the prompt's blocks and copy a block only
+    when they diverge (copy-on-write); beams are forked and discarded.
+
+Readings where the pages are silent:
+  * free blocks form a LIFO stack; the block popped first at start-up is
+    ``init_order[0]`` (``0, 1, ..., NB-1`` by default);
+  * copy-on-write is lazy: ``fork`` copies the table and raises every shared
+    block's count; ``append`` into a last block whose count is above one takes
+    a fresh block, reports the pair (old, new) for the device copy, drops one
+    reference from the old block and points the table at the new one;
+  * ``free`` walks the table from the last logical block to the first,
+    dropping one reference each and pushing every block that reaches zero;
+  * running out of blocks reports ``OOM`` and changes nothing.
+"""
+from __future__ import annotations
+
+
+class OutOfBlocks(Exception):
+    pass
+
+
+class Allocator:
+    def __init__(self, num_blocks: int, bs: int, init_order=None):
+        if num_blocks < 0 or bs < 1:
+            raise ValueError("bad allocator shape")
+        order = list(range(num_blocks)) if init_order is None else [int(b) for b in init_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("init_order must be a permutation of the pool")
+        self.NB = num_blocks
+        self.bs = bs
+        self.free = list(reversed(order))   # top of the stack is the list's end
+        self.ref = [0] * num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.lens: dict[int, int] = {}
+
+    # -- queries -----------------------------------------------------------
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def refcount(self, b: int) -> int:
+        return self.ref[b]
+
+    def seq_len(self, sid: int) -> int:
+        return self.lens[sid]
+
+    def table(self, sid: int) -> list[int]:
+        return list(self.tables[sid])
+
+    def free_stack(self) -> list[int]:
+        """Free blocks in the order they would be handed out."""
+        return list(reversed(self.free))
+
+    # -- sequence operations ----------------------------------------------
+    def create(self, sid: int) -> None:
+        if sid in self.tables:
+            raise KeyError(f"sequence {sid} exists")
+        self.tables[sid] = []
+        self.lens[sid] = 0
+
+    def _pop(self) -> int:
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+    def append(self, sid: int):
+        """Reserve the slot of the sequence's next token.
+
+        Returns ``(slot, cow_src, cow_dst)``; the pair is ``(-1, -1)`` when no
+        block has to be copied before the token is written."""
+        table = self.tables[sid]
+        n = self.lens[sid]
+        off = n % self.bs
+        cow = (-1, -1)
+        if off == 0:                          # last block full (or none yet)
+            if not self.free:
+                raise OutOfBlocks()
+            table.append(self._pop())
+        else:
+            last = table[-1]
+            if self.ref[last] > 1:            # shared: copy before writing
+                if not self.free:
+                    raise OutOfBlocks()
+                new = self._pop()
+                self.ref[last] -= 1
+                table[-1] = new
+                cow = (last, new)
+        self.lens[sid] = n + 1
+        return table[-1] * self.bs + off, cow[0], cow[1]
+
+    def fork(self, parent: int, child: int) -> None:
+        if parent not in self.tables or child in self.tables:
+            raise KeyError("bad fork")
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+
+    def release(self, sid: int) -> None:
+        table = self.tables.pop(sid)
+        del self.lens[sid]
+        for b in reversed(table):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    def build_batch(self, sids, MB: int):
+        """Block tables ``[S][MB]`` (padded with -1) and context lengths."""
+        tables, lens = [], []
+        for sid in sids:
+            t = self.tables[sid]
+            if len(t) > MB:
+                raise ValueError("table wider than MB")
+            tables.append(t + [-1] * (MB - len(t)))
+            lens.append(self.lens[sid])
+        return tables, lens

@@ -1,0 +1,259 @@
+"""Seeded synthetic inputs for the paged decode path.
+
+This module is the one place both sides of a parity check get their inputs
+from.  It draws context lengths, a physical block permutation, block tables
+and N(0,1) query/key/value values; it performs no attention, softmax, slot or
+cache arithmetic.  Everything is a function of ``seed``: integer structure
+(lengths, permutation, tables, tails, allocator start order) comes from
+``numpy.random.default_rng(seed)``, floating-point values from a
+``torch.Generator`` seeded with the same number on the requested device, drawn
+as float32 and rounded to the KV dtype (round-to-nearest-even).
+
+The pages measured on ShareGPT request lengths and LLaMA weights, neither of
+which is available; the length laws below stand in for them (uniform for the
+tiny and long-context cases, lognormal around the stated median for the
+LLaMA-shaped ones), and q/K/V are standard normal.
+
+Pool content convention ("pre-step" pool): a sequence of context length ``ctx``
+has its first ``ctx - 1`` tokens already in the pool; the slot of token
+``ctx - 1`` (the one the decode step writes), the unfilled tail of every last
+block and every block no sequence owns hold NaN, so that any read of them
+shows up in the output.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+KV_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+# Named workloads.  Shapes follow the LLaMA-7B / 13B / 70B attention layers the
+# pages' evaluation is quoted on (page "PagedAttention: the KV cache was the
+# bottleneck all along", section "The number that made us read the code").
+CONFIGS = {
+    "tiny": dict(S=4, Hq=4, Hkv=4, D=64, dtype="f32", bs=16, NB=64,
+                 lengths=("uniform", 1, 100), partition_tokens=0),
+    "llama7b": dict(S=64, Hq=32, Hkv=32, D=128, dtype="f16", bs=16, NB=16384,
+                    lengths=("lognormal", 500, 0.5, 16, 2048), partition_tokens=0),
+    # NB is chosen per block size so that the pool holds 262144 tokens.
+    "llama13b": dict(S=128, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16, NB=None,
+                     pool_tokens=262144, lengths=("lognormal", 700, 0.5, 1, 2048),
+                     partition_tokens=0),
+    "long_gqa": dict(S=8, Hq=64, Hkv=8, D=128, dtype="bf16", bs=16, NB=16384,
+                     lengths=("uniform", 16384, 32768), partition_tokens=512),
+}
+
+SHARED_PREFIX = dict(prompts=16, samples=4, Hq=40, Hkv=40, D=128, dtype="f16", bs=16,
+                     NB=4096, prompt_len=512, tail=(0, 256))
+
+
+def draw_lengths(rng: np.random.Generator, law, S: int) -> np.ndarray:
+    """Context lengths (tokens attended, the step's new token included)."""
+    kind = law[0]
+    if kind == "uniform":
+        lo, hi = law[1], law[2]
+        x = rng.integers(lo, hi + 1, size=S)
+    elif kind == "lognormal":
+        median, sigma, lo, hi = law[1:]
+        x = np.rint(np.exp(rng.normal(np.log(median), sigma, size=S)))
+        x = np.clip(x, lo, hi)
+    elif kind == "fixed":
+        x = np.asarray(law[1], dtype=np.int64)
+        assert x.shape == (S,)
+    else:
+        raise ValueError(f"unknown length law {law!r}")
+    return x.astype(np.int32)
+
+
+def _randn(shape, gen, device, dtype_name: str) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32).to(
+        KV_DTYPES[dtype_name])
+
+
+def _generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+@dataclasses.dataclass
+class DecodeWorkload:
+    """One decode step over a batch of sequences whose K/V live in a paged pool."""
+    name: str
+    seed: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    dtype: str
+    scale: float                 # float32 value handed to both sides
+    partition_tokens: int
+    context_lens: np.ndarray     # int32 [S]
+    block_tables: np.ndarray     # int32 [S, MB], -1 past the sequence's blocks
+    q: torch.Tensor              # [S, Hq, D]
+    key_cache: torch.Tensor      # [NB, Hkv, bs, D] pre-step
+    value_cache: torch.Tensor    # [NB, Hkv, bs, D] pre-step
+    new_key: torch.Tensor        # [S, Hkv, D]  token ctx-1 of each sequence
+    new_value: torch.Tensor      # [S, Hkv, D]
+
+    @property
+    def MB(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.S else 0
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+
+def paged_tables(rng: np.random.Generator, lens: np.ndarray, bs: int, NB: int,
+                 MB: Optional[int] = None) -> np.ndarray:
+    """Assign each sequence ceil(ctx/bs) physical blocks, consecutively from one
+    random permutation of the pool (so neighbours in a table are scattered)."""
+    nblk = (lens.astype(np.int64) + bs - 1) // bs
+    if int(nblk.sum()) > NB:
+        raise ValueError(f"pool of {NB} blocks cannot hold {int(nblk.sum())}")
+    perm = rng.permutation(NB).astype(np.int32)
+    mb = int(nblk.max()) if MB is None else int(MB)
+    tables = np.full((len(lens), max(mb, 1)), -1, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    return tables
+
+
+def filled_mask(tables: np.ndarray, filled: np.ndarray, bs: int, NB: int) -> np.ndarray:
+    """bool [NB, bs]: True where a slot holds one of the first ``filled[s]`` tokens."""
+    mask = np.zeros((NB, bs), dtype=bool)
+    for s in range(tables.shape[0]):
+        n = int(filled[s])
+        j = 0
+        while n > 0:
+            mask[tables[s, j], :min(n, bs)] = True
+            n -= bs
+            j += 1
+    return mask
+
+
+def make_decode(name: str, seed: int = 0, device="cpu", **over) -> DecodeWorkload:
+    """Build a named decode workload; keyword overrides replace config fields
+    (e.g. ``S=6`` for a reduced-size parity case, ``bs=8`` for the sweep)."""
+    cfg = dict(CONFIGS[name])
+    cfg.update(over)
+    S, Hq, Hkv, D, bs = cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["bs"]
+    NB = cfg["NB"] if cfg.get("NB") else cfg["pool_tokens"] // bs
+    rng = np.random.default_rng(seed)
+    lens = draw_lengths(rng, cfg["lengths"], S)
+    tables = paged_tables(rng, lens, bs, NB, cfg.get("MB"))
+    mask = filled_mask(tables, np.maximum(lens.astype(np.int64) - 1, 0), bs, NB)
+    gen = _generator(seed, device)
+    dt = cfg["dtype"]
+    q = _randn((S, Hq, D), gen, device, dt)
+    pools = []
+    poison = ~torch.from_numpy(mask).to(device)[:, None, :, None]
+    for _ in range(2):
+        p = torch.randn(NB, Hkv, bs, D, generator=gen, device=device, dtype=torch.float32)
+        p.masked_fill_(poison, float("nan"))
+        pools.append(p.to(KV_DTYPES[dt]))
+        del p
+    nk = _randn((S, Hkv, D), gen, device, dt)
+    nv = _randn((S, Hkv, D), gen, device, dt)
+    return DecodeWorkload(
+        name=name, seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
+        scale=float(np.float32(1.0 / np.sqrt(D))),
+        partition_tokens=int(cfg.get("partition_tokens", 0)),
+        context_lens=lens, block_tables=tables, q=q,
+        key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
+
+
+@dataclasses.dataclass
+class SharedPrefixScript:
+    """Parallel sampling over shared prompts: each prompt is prefilled into its
+    own sequence, forked into ``samples`` sequences, and every sample then
+    grows by its own tail before one final decode step over all samples."""
+    seed: int
+    prompts: int
+    samples: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    dtype: str
+    scale: float
+    prompt_len: int
+    tails: np.ndarray            # int32 [prompts*samples] tokens appended after the fork
+    init_order: np.ndarray       # int32 [NB] order in which free blocks are handed out
+    prompt_k: torch.Tensor       # [prompts, prompt_len, Hkv, D]
+    prompt_v: torch.Tensor
+    tail_k: torch.Tensor         # [S, max_tail, Hkv, D]
+    tail_v: torch.Tensor
+    step_k: torch.Tensor         # [S, Hkv, D]  final step's token
+    step_v: torch.Tensor
+    q: torch.Tensor              # [S, Hq, D]
+    key_cache: torch.Tensor      # [NB, Hkv, bs, D] initial pool, all NaN
+    value_cache: torch.Tensor
+
+    @property
+    def S(self) -> int:
+        return self.prompts * self.samples
+
+    def seq_id(self, prompt: int, sample: int) -> int:
+        return prompt * self.samples + sample
+
+
+def make_shared_prefix(seed: int = 0, device="cpu", **over) -> SharedPrefixScript:
+    cfg = dict(SHARED_PREFIX)
+    cfg.update(over)
+    rng = np.random.default_rng(seed)
+    P, M = cfg["prompts"], cfg["samples"]
+    S = P * M
+    lo, hi = cfg["tail"]
+    tails = rng.integers(lo, hi + 1, size=S).astype(np.int32)
+    NB = cfg["NB"]
+    init_order = rng.permutation(NB).astype(np.int32)
+    gen = _generator(seed, device)
+    dt, Hkv, Hq, D, L = cfg["dtype"], cfg["Hkv"], cfg["Hq"], cfg["D"], cfg["prompt_len"]
+    mt = int(tails.max()) if S else 0
+    pk = _randn((P, L, Hkv, D), gen, device, dt)
+    pv = _randn((P, L, Hkv, D), gen, device, dt)
+    tk = _randn((S, mt, Hkv, D), gen, device, dt)
+    tv = _randn((S, mt, Hkv, D), gen, device, dt)
+    sk = _randn((S, Hkv, D), gen, device, dt)
+    sv = _randn((S, Hkv, D), gen, device, dt)
+    q = _randn((S, Hq, D), gen, device, dt)
+    kc = torch.full((NB, Hkv, cfg["bs"], D), float("nan"), device=device,
+                    dtype=KV_DTYPES[dt])
+    vc = kc.clone()
+    return SharedPrefixScript(
+        seed=seed, prompts=P, samples=M, Hq=Hq, Hkv=Hkv, D=D, bs=cfg["bs"], NB=NB,
+        dtype=dt, scale=float(np.float32(1.0 / np.sqrt(D))), prompt_len=L, tails=tails,
+        init_order=init_order, prompt_k=pk, prompt_v=pv, tail_k=tk, tail_v=tv,
+        step_k=sk, step_v=sv, q=q, key_cache=kc, value_cache=vc)
+
+
+def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a KV-dtype tensor as its raw storage: float32 / float16 as
+    themselves, bfloat16 as its uint16 bit patterns (numpy has no bfloat16)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def from_numpy_storage(a: np.ndarray, dtype: str, device="cpu") -> torch.Tensor:
+    """Inverse of :func:`to_numpy_storage`."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
