@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of the paged KV path on one MI355X.
+
+A step is the whole hot path over one batch: the cache write of each
+sequence's new token (pa_reshape_and_cache) followed by paged decode
+attention (pa_decode_attention, with its reduce pass when partitioned).
+Inputs are seeded synthetic data already resident in HBM; slots and block
+tables come from the library's host allocator before the timed region.
+
+Default workload: LLaMA-13B-shaped decode layer, 128 sequences, 40 heads of
+128, bfloat16 KV, block size 16, context lengths lognormal (median 700,
+sigma 0.5, at most 2048).  ``value`` is algorithmic KV bytes (every attended
+token's K and V row once per head) per second of whole step.  The
+``roofline`` object prices the decode kernel alone against the 8 TB/s HBM
+peak; ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of
+the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--bs 16] [--partition P]
+                    [--no-sweep] [--no-cpu-baseline] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama13b_bs16.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_198_amd", "csrc", "pa_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--bs", type=int, default=16)
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition tokens (0 = single pass, -1 = library default for the shape)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the plain HBM probe")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def default_partition(bs: int) -> int:
+    return 0
+
+
+class Step:
+    """Device state of one decode step, built once."""
+
+    def __init__(self, pa, synth, torch, bs, seed, partition):
+        self.torch = torch
+        self.pa = pa
+        w = synth.make_decode("llama13b", seed=seed, device="cuda", bs=bs)
+        self.w = w
+        alloc = pa.Allocator(w.NB, w.bs, init_order=w.block_order)
+        step = np.empty(w.S, dtype=np.int64)
+        for s in range(w.S):
+            alloc.create(s)
+            slots, _, _ = alloc.append_n(s, int(w.context_lens[s]))
+            step[s] = slots[-1]
+        tables, lens = alloc.build_batch(list(range(w.S)), w.MB)
+        self.slots = torch.from_numpy(step).cuda()
+        self.tables = torch.from_numpy(tables).cuda()
+        self.lens = torch.from_numpy(lens).cuda()
+        self.max_ctx = int(lens.max())
+        self.part = default_partition(bs) if partition < 0 else partition
+        self.out = torch.empty(w.S, w.Hq, w.D, dtype=w.q.dtype, device="cuda")
+        self.ws = pa.make_workspace(w.S, w.Hq, w.D, self.max_ctx, self.part)
+        self.kv_bytes = int(np.sum(lens.astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
+
+    def write(self):
+        w = self.w
+        self.pa.pa_reshape_and_cache(w.new_key, w.new_value, w.key_cache, w.value_cache,
+                                     self.slots)
+
+    def attend(self):
+        w = self.w
+        self.pa.pa_decode_attention(self.out, w.q, w.key_cache, w.value_cache, self.tables,
+                                    self.lens, self.max_ctx, w.scale, self.part, self.ws)
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.write()
+            self.attend()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for a, b in ev:
+            self.write()
+            a.record()
+            self.attend()
+            b.record()
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = start.elapsed_time(stop) / steps
+        attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        return step_ms, attn_ms, wall
+
+
+def traffic_bytes():
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if t.get("kernel_source_sha256") != sha:
+        return None
+    return float(t["bytes_per_launch"])
+
+
+def cpu_baseline(step, budget_s=10.0):
+    """The float64 oracle on the host, on the first sequences of the same
+    workload until about ``budget_s`` seconds of work."""
+    import oracle.decode as od
+    from paged_kv_cache_198_amd import synth
+    torch = step.torch
+    w = step.w
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+
+    def run(seqs):
+        need = [-(-int(w.context_lens[s]) // w.bs) for s in seqs]
+        blocks = np.unique(np.concatenate([w.block_tables[s, :n] for s, n in zip(seqs, need)]))
+        remap = np.full(w.NB, -1, dtype=np.int64)
+        remap[blocks] = np.arange(len(blocks))
+        idx = torch.from_numpy(blocks.astype(np.int64)).cuda()
+        kc = synth.to_numpy_storage(w.key_cache.index_select(0, idx))
+        vc = synth.to_numpy_storage(w.value_cache.index_select(0, idx))
+        tab = np.where(w.block_tables[seqs] >= 0, remap[np.maximum(w.block_tables[seqs], 0)], -1)
+        q = synth.to_numpy_storage(w.q[seqs])
+        t0 = time.perf_counter()
+        od.paged_decode(q, kc, vc, tab, w.context_lens[seqs], w.scale, w.dtype)
+        return time.perf_counter() - t0
+
+    probe = run([0])
+    per_seq = max(probe, 1e-3)
+    n = int(min(w.S, max(1, budget_s / per_seq)))
+    seqs = list(range(n))
+    kv = int(np.sum(w.context_lens[seqs].astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
+    secs, reps = 0.0, 0
+    while reps == 0 or (secs < budget_s and reps < 50):
+        secs += run(seqs)
+        reps += 1
+    return {"value": kv * reps / secs / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} of {w.S} sequences ({kv / 1e9:.3f} GB of KV) x {reps} "
+                      f"passes, {secs:.1f} s, float64 numpy"}
+
+
+def hbm_probe(torch, gib=4, reps=10):
+    """Plain device-memory rates on this machine from torch's own kernels: a copy
+    (read + write) and a sum (read only) over ``gib`` GiB; context for the
+    fraction of the 8 TB/s peak the decode kernel reaches."""
+    n = gib << 30
+    a = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * n), ("sum", lambda: a.sum(), n)):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out[f"torch_{name}_GBs"] = moved * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def calibrate_copy(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_198_amd as pa
+    from paged_kv_cache_198_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pa.lib()
+    print(f"[bench] building workload llama13b bs={args.bs}", file=sys.stderr, flush=True)
+    st = Step(pa, synth, torch, args.bs, args.seed, args.partition)
+    w = st.w
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
+    step_ms, attn_ms, wall = st.run(args.steps, args.warmup)
+
+    sweep = {}
+    if not args.no_sweep:
+        for bs in (8, 16, 32):
+            if bs == args.bs:
+                continue
+            print(f"[bench] sweep bs={bs}", file=sys.stderr, flush=True)
+            other = Step(pa, synth, torch, bs, args.seed, args.partition)
+            s_ms, a_ms, _ = other.run(max(20, args.steps // 4), args.warmup)
+            sweep[f"bs{bs}"] = {"us_per_step": s_ms * 1e3, "attention_us": a_ms * 1e3,
+                                "attention_GBs": other.kv_bytes / (a_ms * 1e-3) / 1e9,
+                                "frac_hbm_peak": other.kv_bytes / (a_ms * 1e-3) / 1e9
+                                / HBM_PEAK_GBS}
+            del other
+            torch.cuda.empty_cache()
+
+    achieved = st.kv_bytes / (attn_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode-attention KV GB/s (frac of MI355X HBM peak) + us/step, "
+                  "13B-shaped batch",
+        "value": st.kv_bytes / (step_ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "us_per_step": step_ms * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, lognormal context lengths)",
+        "config": {
+            "workload": f"LLaMA-13B-shaped decode layer: S={w.S}, Hq=Hkv={w.Hkv}, D={w.D}, "
+                        f"{w.dtype} KV, block_size {w.bs}, ctx lognormal(700, 0.5) in "
+                        f"[1, 2048], {w.NB}-block pool shuffled, 1 new token per sequence",
+            "S": w.S, "heads": w.Hq, "head_dim": w.D, "block_size": w.bs,
+            "tokens": int(np.sum(w.context_lens)), "kv_bytes": st.kv_bytes,
+            "partition_tokens": st.part, "seed": args.seed,
+        },
+        "attention_us": attn_ms * 1e3,
+        "frac_hbm_peak_step": st.kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_bytes(),
+            "kernel": "pa::decode_kernel" + (" + reduce_kernel" if st.part else ""),
+            "algorithmic_bytes_per_launch": st.kv_bytes,
+        },
+        "sweep": sweep,
+        "wall_s_timed": wall,
+    }
+    if not args.no_probe:
+        line["hbm_probe"] = hbm_probe(torch)
+        best = max(line["hbm_probe"].values())
+        line["roofline"]["frac_of_probe"] = achieved / best
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(st)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV cache decode path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What is computed.  "PagedAttention: the KV cache was the bottleneck all
+ * along", section "Virtual memory for attention": the KV cache is cut into
+ * fixed-size blocks holding the keys and values of a fixed number of tokens;
+ * a per-sequence block table maps logical blocks to physical blocks that need
+ * not be adjacent, as a page table maps virtual to physical pages; a sequence
+ * acquires blocks as it grows; the attention kernel gathers keys and values
+ * from the scattered blocks; completions of one prompt share its blocks and
+ * copy one only when they diverge (copy-on-write).  The abstract of
+ * "Efficient Memory Management for Large Language Model Serving with
+ * PagedAttention" names the same two properties (near-zero KV waste,
+ * sharing within and across requests).
+ *
+ * Data layout (the pages fix none; these are this library's choices):
+ *   KV pool, one per layer and per K / V:  [NB][Hkv][bs][D] elements, dense,
+ *     16-byte aligned.  Block b is the index b in both the key and the value
+ *     pool.  Token slot = block * bs + offset.
+ *   query / output:                         [S][Hq][D], dense.
+ *   new keys / values for the cache write:  [T][Hkv][D], dense.
+ *   block tables:                           int32 [S][MB], row s lists the
+ *     physical blocks of sequence s in logical order; entries past
+ *     ceil(context_lens[s] / bs) are ignored (conventionally -1).
+ *   context lengths:                        int32 [S], tokens attended,
+ *     including the token being decoded.
+ * Element types: PA_F32, PA_F16 (IEEE half), PA_BF16 (bfloat16); the query,
+ * the pools and the output share one type; arithmetic is float32.
+ *
+ * Ownership and synchronisation.  Every device buffer is allocated and freed
+ * by the caller.  Device entry points only enqueue work on `stream` (a
+ * hipStream_t passed as void*; NULL is the null stream) and return without
+ * waiting; they never allocate device memory.  The allocator owns host
+ * memory only and is not thread-safe (one scheduler thread per allocator).
+ *
+ * Errors.  Arguments are checked before anything is enqueued; on a non-zero
+ * status nothing was launched.  PA_ERR_HIP reports a failed launch
+ * (hipGetLastError after the launch).  Device code never traps: values that
+ * cannot be checked on the host (table entries, slots, lengths held in device
+ * memory) are clamped or skipped so that every access stays inside the
+ * buffers whose sizes the call states; the affected results are then
+ * unspecified.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument (shape, pointer, id, value)      */
+  PA_ERR_OOM = -2,         /* allocator has no free block; state unchanged  */
+  PA_ERR_HIP = -3,         /* HIP reported an error for a launch            */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required    */
+  PA_ERR_UNSUPPORTED = -5  /* valid shape outside the compiled set          */
+};
+
+/* Library version (major*10000 + minor*100 + patch). */
+int pa_version(void);
+
+/* Human-readable text for a status code (static storage). */
+const char* pa_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Cache write.  Places each new token's key and value rows in its slot
+ * ("Virtual memory for attention": a growing sequence's tokens go into the
+ * blocks its table names).
+ *   key, value       device, [T][Hkv][D] of `dtype`.
+ *   key_cache,
+ *   value_cache      device, [NB][Hkv][bs][D]; written in place.
+ *   slot_mapping     device int64 [T]: token t goes to block slot/bs, offset
+ *                    slot%bs, for every head.  -1 = no write.  A slot outside
+ *                    [0, NB*bs) is skipped.  Two tokens with one slot: the
+ *                    stored row is one of them, unspecified which.
+ * Supported: D in {64, 128}, any bs >= 1, T >= 0 (T = 0 enqueues nothing). */
+int pa_reshape_and_cache(const void* key, const void* value,
+                         void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping,
+                         int32_t T, int32_t Hkv, int32_t D, int32_t bs, int32_t NB,
+                         int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over paged keys and values: for every sequence s and
+ * query head h, with g = h / (Hq / Hkv),
+ *     out[s][h] = softmax_j(scale * q[s][h] . K_s[j][g]) . V_s[j][g],
+ * j over the first context_lens[s] logical tokens, K_s / V_s read through
+ * the block table row s ("Virtual memory for attention": gather keys and
+ * values from scattered blocks).
+ *
+ * Split context.  partition_tokens = 0 reads each sequence in one pass.
+ * partition_tokens = P > 0 (a multiple of 256) cuts each context into
+ * P-token partitions, one workgroup each, which write their softmax max,
+ * sum and unnormalised output to `workspace`; a second kernel combines
+ * them.  Sequences that fit one partition are written directly.
+ *
+ *   out              device [S][Hq][D] of `dtype`.
+ *   query            device [S][Hq][D] of `dtype`.
+ *   key_cache,
+ *   value_cache      device [NB][Hkv][bs][D].
+ *   block_tables     device int32 [S][MB].  An entry outside [0, NB) that
+ *                    falls inside the context is skipped (its tokens do not
+ *                    take part); the output for that sequence is then
+ *                    unspecified.
+ *   context_lens     device int32 [S].  Values are clamped to
+ *                    [0, min(max_context_len, MB*bs)]; a sequence with 0
+ *                    tokens gets an all-zero output.
+ *   max_context_len  host bound on context_lens (sizes the grid and the
+ *                    workspace), >= 1.
+ *   scale            logit scale (e.g. 1/sqrt(D)).
+ *   workspace        device, at least pa_decode_workspace_bytes(...) bytes,
+ *                    256-byte aligned; may be NULL when that size is 0.
+ * Supported: dtype any; D in {64, 128}; bs in {8, 16, 32};
+ *            Hq / Hkv in {1, 2, 4, 8}. */
+size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+int pa_decode_attention(void* out, const void* query,
+                        const void* key_cache, const void* value_cache,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                        int32_t bs, int32_t NB, int32_t MB,
+                        int32_t max_context_len, float scale,
+                        int32_t partition_tokens,
+                        void* workspace, size_t workspace_bytes,
+                        int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Block copy for copy-on-write ("Virtual memory for attention": a completion
+ * that diverges from a shared block gets its own copy).  For every pair
+ * (src, dst) and every layer l, key block dst becomes a copy of key block
+ * src, and value block dst of value block src.
+ *   key_caches,
+ *   value_caches     HOST arrays of L device pointers, one pool per layer.
+ *   block_mapping    HOST int64 [n][2] of (src, dst).  Every block in
+ *                    [0, NB); src != dst; no block is the dst of two pairs;
+ *                    no dst is also a src.  Under these rules the pairs are
+ *                    independent, so the result is that of applying them in
+ *                    order.  Violations return PA_ERR_INVALID.
+ *   block_bytes      bytes of one block in one pool (bs*Hkv*D*elem), a
+ *                    positive multiple of 16.
+ * n = 0 or L = 0 enqueues nothing. */
+int pa_copy_blocks(void* const* key_caches, void* const* value_caches, int32_t L,
+                   const int64_t* block_mapping, int32_t n, int32_t NB,
+                   int64_t block_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator ("Virtual memory for attention": blocks acquired as a
+ * sequence grows, refcounted sharing, copy-on-write, forked and discarded
+ * sequences).  Rules where the pages are silent:
+ *   - free blocks form a LIFO stack; init_order[0] is handed out first
+ *     (NULL: 0, 1, ..., NB-1);
+ *   - copy-on-write is lazy: fork copies the table and adds a reference to
+ *     every block; an append into a partly filled last block with more than
+ *     one reference takes a fresh block, returns (old, new) to be copied on
+ *     the device before the token is written, and drops one reference from
+ *     the old block; a full shared block is never copied;
+ *   - free walks the table from the last logical block to the first,
+ *     dropping a reference each and pushing every block that reaches zero;
+ *   - PA_ERR_OOM leaves the allocator unchanged.
+ * Sequence ids are arbitrary int64 values. */
+typedef struct pa_allocator pa_allocator;
+
+/* NULL on a bad argument (NB < 0, bs < 1, init_order not a permutation). */
+pa_allocator* pa_alloc_create(int32_t num_blocks, int32_t bs, const int32_t* init_order);
+void pa_alloc_destroy(pa_allocator* a);
+int32_t pa_alloc_num_free(const pa_allocator* a);
+int32_t pa_alloc_num_blocks(const pa_allocator* a);
+int32_t pa_alloc_block_size(const pa_allocator* a);
+/* -1 for a block outside the pool. */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
+
+int pa_seq_create(pa_allocator* a, int64_t seq_id);
+/* Reserve the slot of the sequence's next token.  *cow_src / *cow_dst get
+ * the block pair to copy first, or -1 / -1. */
+int pa_seq_append(pa_allocator* a, int64_t seq_id, int64_t* slot,
+                  int64_t* cow_src, int64_t* cow_dst);
+/* n appends at once (a prompt): slots[0..n) filled; at most the first can
+ * need a copy, reported in *cow_src / *cow_dst.  All or nothing. */
+int pa_seq_append_n(pa_allocator* a, int64_t seq_id, int32_t n, int64_t* slots,
+                    int64_t* cow_src, int64_t* cow_dst);
+int pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+int pa_seq_free(pa_allocator* a, int64_t seq_id);
+/* -1 for an unknown id. */
+int32_t pa_seq_len(const pa_allocator* a, int64_t seq_id);
+int32_t pa_seq_num_blocks(const pa_allocator* a, int64_t seq_id);
+/* Copies the sequence's block table into blocks[0..pa_seq_num_blocks). */
+int pa_seq_blocks(const pa_allocator* a, int64_t seq_id, int32_t* blocks, int32_t cap);
+
+/* Host block tables [S][MB] (padded with -1) and context lengths [S] for a
+ * batch of sequences.  PA_ERR_INVALID if a table is wider than MB. */
+int pa_build_batch(const pa_allocator* a, const int64_t* seq_ids, int32_t S, int32_t MB,
+                   int32_t* block_tables, int32_t* context_lens);
+
+/* Snapshot: refcounts[NB]; free_stack[n] in hand-out order (first = next). */
+int pa_alloc_export(const pa_allocator* a, int32_t* refcounts, int32_t* free_stack,
+                    int32_t* n_free);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,315 @@
+"""Paged KV cache decode path for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libpa.so`` (C ABI in ``include/pa.h``).  The
+functions below only check and marshal arguments (torch tensors -> device
+pointers and sizes, the current torch stream -> hipStream_t); every step of
+the computation runs in the library's HIP kernels or its C++ allocator.  There
+is no fallback: if ``libpa.so`` is missing, every call raises.
+
+Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_decode_attention``,
+``pa_decode_workspace_bytes``, ``pa_copy_blocks``; ``Allocator`` wraps the
+``pa_alloc_*`` / ``pa_seq_*`` calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch  # loads the HIP runtime libpa.so then binds to (one runtime per process)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+_ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2}
+
+PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNSUPPORTED = (
+    0, -1, -2, -3, -4, -5)
+
+_lib = None
+
+_c_int, _c_i32, _c_i64, _c_p = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_p_i32 = ctypes.POINTER(ctypes.c_int32)
+_p_i64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "pa_version": (_c_int, []),
+    "pa_status_string": (ctypes.c_char_p, [_c_int]),
+    "pa_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _c_i32, _c_p]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_attention": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                     _c_i32, _c_p, ctypes.c_size_t, _c_i32, _c_p]),
+    "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
+                                _c_i32, _c_i32, _c_i64, _c_p]),
+    "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
+    "pa_alloc_destroy": (None, [_c_p]),
+    "pa_alloc_num_free": (_c_i32, [_c_p]),
+    "pa_alloc_num_blocks": (_c_i32, [_c_p]),
+    "pa_alloc_block_size": (_c_i32, [_c_p]),
+    "pa_alloc_refcount": (_c_i32, [_c_p, _c_i32]),
+    "pa_seq_create": (_c_int, [_c_p, _c_i64]),
+    "pa_seq_append": (_c_int, [_c_p, _c_i64, _p_i64, _p_i64, _p_i64]),
+    "pa_seq_append_n": (_c_int, [_c_p, _c_i64, _c_i32, _p_i64, _p_i64, _p_i64]),
+    "pa_seq_fork": (_c_int, [_c_p, _c_i64, _c_i64]),
+    "pa_seq_free": (_c_int, [_c_p, _c_i64]),
+    "pa_seq_len": (_c_i32, [_c_p, _c_i64]),
+    "pa_seq_num_blocks": (_c_i32, [_c_p, _c_i64]),
+    "pa_seq_blocks": (_c_int, [_c_p, _c_i64, _p_i32, _c_i32]),
+    "pa_build_batch": (_c_int, [_c_p, _p_i64, _c_i32, _c_i32, _p_i32, _p_i32]),
+    "pa_alloc_export": (_c_int, [_c_p, _p_i32, _p_i32, _p_i32]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class OutOfBlocks(PaError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_198_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(status).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc == PA_ERR_OOM:
+        raise OutOfBlocks(rc, where)
+    if rc != PA_OK:
+        raise PaError(rc, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"unsupported KV dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+# ---------------------------------------------------------------------------
+# device operations
+# ---------------------------------------------------------------------------
+def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                         stream=None) -> None:
+    """Write each token's key/value rows ([T, Hkv, D]) into its slot of the
+    [NB, Hkv, bs, D] pools; slot -1 = no write."""
+    dt = _kv_dtype(key_cache)
+    NB, Hkv, bs, D = key_cache.shape
+    T = key.shape[0]
+    for name, t in (("key", key), ("value", value)):
+        if tuple(t.shape) != (T, Hkv, D) or t.dtype != key_cache.dtype:
+            raise ValueError(f"{name} must be [T, {Hkv}, {D}] {key_cache.dtype}")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    rc = lib().pa_reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        T, Hkv, D, bs, NB, dt, _stream(stream))
+    _check(rc, "pa_reshape_and_cache")
+
+
+def pa_decode_workspace_bytes(S: int, Hq: int, D: int, max_context_len: int,
+                              partition_tokens: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(S, Hq, D, max_context_len, partition_tokens))
+
+
+def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, max_context_len: int, scale: float,
+                        partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """Paged single-query decode attention; ``out`` and ``query`` are
+    [S, Hq, D] in the pools' dtype."""
+    dt = _kv_dtype(key_cache)
+    NB, Hkv, bs, D = key_cache.shape
+    S, Hq, Dq = query.shape
+    if Dq != D or query.dtype != key_cache.dtype:
+        raise ValueError("query must be [S, Hq, D] in the KV dtype")
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != key_cache.dtype:
+        raise ValueError("out must be [S, Hq, D] in the KV dtype")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, MB]")
+    if tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be [S]")
+    MB = block_tables.shape[1]
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().pa_decode_attention(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
+        _stream(stream))
+    _check(rc, "pa_decode_attention")
+
+
+def make_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_tokens: int,
+                   device="cuda") -> Optional[torch.Tensor]:
+    """A workspace tensor of the required size (None when none is needed)."""
+    n = pa_decode_workspace_bytes(S, Hq, D, max_context_len, partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pa_copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],
+                   block_mapping, stream=None) -> None:
+    """Copy-on-write copies: for each (src, dst) in ``block_mapping`` (host
+    int64 [n, 2]), block dst of every layer's K and V pool becomes a copy of
+    block src."""
+    L = len(key_caches)
+    if len(value_caches) != L:
+        raise ValueError("one value pool per key pool")
+    pairs = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    n = pairs.shape[0]
+    if L == 0 or n == 0:
+        return
+    ref = key_caches[0]
+    NB = ref.shape[0]
+    block_bytes = ref[0].numel() * ref.element_size()
+    for t in list(key_caches) + list(value_caches):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("all pools must have one shape and dtype")
+    kp = (_c_p * L)(*[_dev(t, "key_caches") for t in key_caches])
+    vp = (_c_p * L)(*[_dev(t, "value_caches") for t in value_caches])
+    rc = lib().pa_copy_blocks(kp, vp, L, pairs.ctypes.data_as(_p_i64), n, NB, block_bytes,
+                              _stream(stream))
+    _check(rc, "pa_copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+# ---------------------------------------------------------------------------
+class Allocator:
+    """Host block allocator (C++): free list, refcounts, copy-on-write fork."""
+
+    def __init__(self, num_blocks: int, bs: int, init_order=None):
+        L = lib()
+        order = None
+        if init_order is not None:
+            self._order = np.ascontiguousarray(np.asarray(init_order, dtype=np.int32))
+            if self._order.shape != (num_blocks,):
+                raise ValueError("init_order must have num_blocks entries")
+            order = self._order.ctypes.data_as(_p_i32)
+        self._h = L.pa_alloc_create(num_blocks, bs, order)
+        if not self._h:
+            raise PaError(PA_ERR_INVALID, "pa_alloc_create")
+        self.num_blocks = num_blocks
+        self.bs = bs
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def num_free(self) -> int:
+        return lib().pa_alloc_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return lib().pa_alloc_refcount(self._h, block)
+
+    def create(self, seq_id: int) -> None:
+        _check(lib().pa_seq_create(self._h, seq_id), "pa_seq_create")
+
+    def append(self, seq_id: int):
+        """(slot, cow_src, cow_dst) for the sequence's next token."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_seq_append(self._h, seq_id, ctypes.byref(slot), ctypes.byref(src),
+                                   ctypes.byref(dst)), "pa_seq_append")
+        return slot.value, src.value, dst.value
+
+    def append_n(self, seq_id: int, n: int):
+        """(slots[n] int64, cow_src, cow_dst)."""
+        slots = np.empty(n, dtype=np.int64)
+        src, dst = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_seq_append_n(self._h, seq_id, n, slots.ctypes.data_as(_p_i64),
+                                     ctypes.byref(src), ctypes.byref(dst)), "pa_seq_append_n")
+        return slots, src.value, dst.value
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib().pa_seq_fork(self._h, parent, child), "pa_seq_fork")
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_seq_free(self._h, seq_id), "pa_seq_free")
+
+    def seq_len(self, seq_id: int) -> int:
+        return lib().pa_seq_len(self._h, seq_id)
+
+    def seq_blocks(self, seq_id: int) -> list:
+        n = lib().pa_seq_num_blocks(self._h, seq_id)
+        if n < 0:
+            raise PaError(PA_ERR_INVALID, "pa_seq_num_blocks")
+        buf = np.empty(max(n, 1), dtype=np.int32)
+        _check(lib().pa_seq_blocks(self._h, seq_id, buf.ctypes.data_as(_p_i32), n),
+               "pa_seq_blocks")
+        return buf[:n].tolist()
+
+    def build_batch(self, seq_ids, MB: int):
+        """(block_tables int32 [S, MB] padded with -1, context_lens int32 [S]), host."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        S = ids.shape[0]
+        tables = np.empty((S, MB), dtype=np.int32)
+        lens = np.empty(S, dtype=np.int32)
+        _check(lib().pa_build_batch(self._h, ids.ctypes.data_as(_p_i64), S, MB,
+                                    tables.ctypes.data_as(_p_i32), lens.ctypes.data_as(_p_i32)),
+               "pa_build_batch")
+        return tables, lens
+
+    def export(self):
+        """(refcounts [NB], free blocks in hand-out order)."""
+        ref = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        free = np.empty(max(self.num_blocks, 1), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_alloc_export(self._h, ref.ctypes.data_as(_p_i32),
+                                     free.ctypes.data_as(_p_i32), ctypes.byref(n)),
+               "pa_alloc_export")
+        return ref[:self.num_blocks].tolist(), free[:n.value].tolist()

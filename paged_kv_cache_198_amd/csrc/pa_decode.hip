@@ -1,0 +1,481 @@
+// Paged single-query decode attention for gfx950 (CDNA4).
+//
+// "PagedAttention: the KV cache was the bottleneck all along", section
+// "Virtual memory for attention": each sequence's keys and values sit in
+// fixed-size blocks scattered over the pool, found through its block table,
+// and the attention kernel gathers them from there.  The attention itself is
+// the textbook single-query softmax(scale * q.K^T).V.
+//
+// Work decomposition.  One workgroup of kWaves wavefronts per
+// (KV head, sequence, context partition); the G query heads that share the KV
+// head are all handled by that workgroup, so each K/V byte is read once.
+//
+// Data path inside a workgroup.  A token row of one head is D*elem bytes =
+// RL lanes x 16 bytes (RL = 16 for D=128 at 2 bytes), so one dwordx4 load
+// instruction of a wavefront fetches RPW = 64/RL whole token rows, contiguous
+// inside one block.  Each lane keeps, for its 16-byte column chunk, the query
+// elements of the G heads (pre-multiplied by scale*log2(e) so exp2 can be
+// used), and an online-softmax state (running max m, sum l, output acc) per
+// row group: the RPW row groups of a wave and the waves of a workgroup are
+// independent partial softmaxes, merged once at the end (first across row
+// groups with cross-lane shuffles, then across waves through LDS).  The q.k
+// partial dot products are summed over the RL lanes of a row with DPP
+// (quad_perm, row_half_mirror, row_mirror; ds_swizzle for 32 lanes), which
+// leaves the full dot product in every lane of the row.
+//
+// Block-table entries for the workgroup's range are staged in LDS once per
+// chunk of kTableChunk blocks; K/V rows go straight from HBM to registers
+// (each byte is consumed by exactly one lane, so an LDS hop would add traffic
+// without reuse).  Tokens past the context are never loaded: their loads are
+// predicated off and their weights are exactly zero.
+//
+// Split context.  With partition_tokens > 0 each partition writes
+// (m, l, unnormalised acc) in float32 to the workspace and reduce_kernel
+// combines them: M = max_p m_p, out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+// A sequence that fits in one partition is written directly.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kWaves = 4;
+constexpr int kTableChunk = 1024;
+
+template <int DT> struct KV;
+template <> struct KV<PA_F32> { using T = float; static constexpr int kBytes = 4; };
+template <> struct KV<PA_F16> { using T = _Float16; static constexpr int kBytes = 2; };
+template <> struct KV<PA_BF16> { using T = uint16_t; static constexpr int kBytes = 2; };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes of stored elements -> float32.
+template <int DT>
+__device__ __forceinline__ void widen16(const uint4& c, float* f) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  if constexpr (DT == PA_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, w[i]);
+  } else if constexpr (DT == PA_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2_t h = __builtin_bit_cast(half2_t, w[i]);
+      f[2 * i] = static_cast<float>(h.x);
+      f[2 * i + 1] = static_cast<float>(h.y);
+    }
+  } else {
+    // bfloat16 is the upper half of a float32.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    }
+  }
+}
+
+// float32 -> stored element, round to nearest even.
+template <int DT>
+__device__ __forceinline__ typename KV<DT>::T narrow(float x) {
+  if constexpr (DT == PA_F32) {
+    return x;
+  } else if constexpr (DT == PA_F16) {
+    return static_cast<_Float16>(x);
+  } else {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  }
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over the RL consecutive lanes of a token row; every lane of the row
+// ends with the same value (each step adds a value and its partner's, and
+// float addition is commutative).
+template <int RL>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(RL == 8 || RL == 16 || RL == 32, "row width");
+  x += dpp<0xb1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4e>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror: quads 0<->1 of each 8
+  if constexpr (RL >= 16) x += dpp<0x140>(x);  // row_mirror: halves of a 16-lane row
+  if constexpr (RL >= 32)                      // lane ^ 16 inside each 32
+    x += __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_m;
+  float* ws_l;
+  float* ws_o;
+  int32_t S, Hq, Hkv, NB, MB, max_ctx;
+  int32_t part_tokens;  // 0: one pass over the whole context
+  int32_t pmax;         // partitions per sequence in the grid / workspace
+  float qscale;         // scale * log2(e)
+};
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s, int bs) {
+  const int c = a.context_lens[s];
+  return max(0, min(c, min(a.max_ctx, a.MB * bs)));
+}
+
+template <int DT, int D, int BS, int G>
+__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+  using T = typename KV<DT>::T;
+  constexpr int EB = KV<DT>::kBytes;
+  constexpr int VEC = 16 / EB;           // elements per lane chunk
+  constexpr int RL = D * EB / 16;        // lanes per token row
+  constexpr int RPW = 64 / RL;           // token rows per wave load
+  constexpr int NL = (G >= 4) ? 4 : 8;   // rows per lane per tile
+  constexpr int TILE = NL * RPW;         // tokens per wave per tile
+  constexpr float kNegInf = -INFINITY;
+
+  __shared__ int32_t tbl[kTableChunk];
+  __shared__ float red_acc[kWaves][G][D];
+  __shared__ float red_m[kWaves][G];
+  __shared__ float red_l[kWaves][G];
+
+  const int g = blockIdx.x;
+  const int s = blockIdx.y;
+  const int p = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = lane / RL;
+  const int c = lane - r * RL;
+
+  const int ctx = clamp_ctx(a, s, BS);
+  const int PT = a.part_tokens > 0 ? a.part_tokens : max(ctx, 1);
+  const int nparts = max(1, (ctx + PT - 1) / PT);
+  if (p >= nparts) return;
+  const int start = p * PT;
+  const int end = min(ctx, start + PT);
+
+  float qf[G][VEC];
+  {
+    const T* qb = static_cast<const T*>(a.q) + (static_cast<size_t>(s) * a.Hq + g * G) * D + c * VEC;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      widen16<DT>(*reinterpret_cast<const uint4*>(qb + gi * D), qf[gi]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qf[gi][e] *= a.qscale;
+    }
+  }
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    m[gi] = kNegInf;
+    l[gi] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[gi][e] = 0.f;
+  }
+
+  const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.MB;
+  const size_t block_stride = static_cast<size_t>(a.Hkv) * BS * D;
+  const T* kb = static_cast<const T*>(a.key_cache) + static_cast<size_t>(g) * BS * D + c * VEC;
+  const T* vb = static_cast<const T*>(a.value_cache) + static_cast<size_t>(g) * BS * D + c * VEC;
+
+  for (int cs = start; cs < end; cs += kTableChunk * BS) {
+    const int ce = min(end, cs + kTableChunk * BS);
+    const int b0 = cs / BS;
+    const int nb = (ce - 1) / BS - b0 + 1;
+    __syncthreads();
+    for (int i = tid; i < nb; i += kWaves * 64) tbl[i] = trow[b0 + i];
+    __syncthreads();
+
+    for (int t0 = cs + w * TILE; t0 < ce; t0 += kWaves * TILE) {
+      uint4 kr[NL], vr[NL];
+      bool ok[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int t = t0 + j * RPW + r;
+        const int bi = min(t / BS - b0, nb - 1);
+        const int blk = tbl[bi];
+        ok[j] = t < ce && static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
+        const size_t off = static_cast<size_t>(blk) * block_stride + static_cast<size_t>(t % BS) * D;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (ok[j]) {
+          kv = *reinterpret_cast<const uint4*>(kb + off);
+          vv = *reinterpret_cast<const uint4*>(vb + off);
+        }
+        kr[j] = kv;
+        vr[j] = vv;
+      }
+
+      // logits (log2 domain) for the NL rows of this lane, every head
+      float sc[NL][G];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        float kf[VEC];
+        widen16<DT>(kr[j], kf);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) d = fmaf(qf[gi][e], kf[e], d);
+          sc[j][gi] = row_sum<RL>(d);
+        }
+      }
+
+      // online softmax: rescale once per tile, then accumulate
+      float pw[NL][G];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float mt = kNegInf;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) mt = ok[j] ? fmaxf(mt, sc[j][gi]) : mt;
+        const float mn = fmaxf(m[gi], mt);
+        const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[gi] - mn);
+        l[gi] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[gi][e] *= alpha;
+        m[gi] = mn;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          pw[j][gi] = ok[j] ? fast_exp2(sc[j][gi] - mn) : 0.f;
+          l[gi] += pw[j][gi];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        float vf[VEC];
+        widen16<DT>(vr[j], vf);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[gi][e] = fmaf(pw[j][gi], vf[e], acc[gi][e]);
+      }
+    }
+  }
+
+  // merge the RPW row groups of the wave
+#pragma unroll
+  for (int off = RL; off < 64; off <<= 1) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const float mo = __shfl_xor(m[gi], off);
+      const float lo = __shfl_xor(l[gi], off);
+      const float mn = fmaxf(m[gi], mo);
+      const float sa = (m[gi] == kNegInf) ? 0.f : fast_exp2(m[gi] - mn);
+      const float sb = (mo == kNegInf) ? 0.f : fast_exp2(mo - mn);
+      l[gi] = l[gi] * sa + lo * sb;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[gi][e], off);
+        acc[gi][e] = acc[gi][e] * sa + ao * sb;
+      }
+      m[gi] = mn;
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red_acc[w][gi][c * VEC + e] = acc[gi][e];
+      if (c == 0) {
+        red_m[w][gi] = m[gi];
+        red_l[w][gi] = l[gi];
+      }
+    }
+  }
+  __syncthreads();
+
+  // merge the waves; one thread per (head, element)
+  for (int i = tid; i < G * D; i += kWaves * 64) {
+    const int gi = i / D;
+    const int d = i - gi * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, red_m[v][gi]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = red_m[v][gi];
+      const float sw = (mv == kNegInf) ? 0.f : fast_exp2(mv - M);
+      num = fmaf(red_acc[v][gi][d], sw, num);
+      den = fmaf(red_l[v][gi], sw, den);
+    }
+    const int h = g * G + gi;
+    if (nparts == 1) {
+      static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * D + d] =
+          narrow<DT>(den > 0.f ? num / den : 0.f);
+    } else {
+      const size_t idx = (static_cast<size_t>(s) * a.Hq + h) * a.pmax + p;
+      a.ws_o[idx * D + d] = num;
+      if (d == 0) {
+        a.ws_m[idx] = M;
+        a.ws_l[idx] = den;
+      }
+    }
+  }
+}
+
+// Combine the partitions of sequences longer than one partition.
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
+  using T = typename KV<DT>::T;
+  constexpr float kNegInf = -INFINITY;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int d = threadIdx.x;
+  const int ctx = clamp_ctx(a, s, BS);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (nparts <= 1) return;
+  const size_t base = (static_cast<size_t>(s) * a.Hq + h) * a.pmax;
+  float M = kNegInf;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_m[base + p]);
+  float num = 0.f, den = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float mp = a.ws_m[base + p];
+    const float sw = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
+    num = fmaf(a.ws_o[(base + p) * D + d], sw, num);
+    den = fmaf(a.ws_l[base + p], sw, den);
+  }
+  static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * D + d] =
+      narrow<DT>(den > 0.f ? num / den : 0.f);
+}
+
+template <int DT, int D, int BS, int G>
+int launch_decode(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<DT, D, BS, G>),
+                     dim3(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
+                          static_cast<uint32_t>(a.pmax)),
+                     dim3(kWaves * 64), 0, st, a);
+  if (a.part_tokens > 0 && a.pmax > 1)
+    hipLaunchKernelGGL((reduce_kernel<DT, D, BS>),
+                       dim3(static_cast<uint32_t>(a.Hq), static_cast<uint32_t>(a.S)), dim3(D), 0,
+                       st, a);
+  return launch_status();
+}
+
+template <int DT, int D, int BS>
+int dispatch_g(const DecodeArgs& a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_decode<DT, D, BS, 1>(a, st);
+    case 2: return launch_decode<DT, D, BS, 2>(a, st);
+    case 4: return launch_decode<DT, D, BS, 4>(a, st);
+    case 8: return launch_decode<DT, D, BS, 8>(a, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+template <int DT, int D>
+int dispatch_bs(const DecodeArgs& a, int bs, int G, hipStream_t st) {
+  switch (bs) {
+    case 8: return dispatch_g<DT, D, 8>(a, G, st);
+    case 16: return dispatch_g<DT, D, 16>(a, G, st);
+    case 32: return dispatch_g<DT, D, 32>(a, G, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+template <int DT>
+int dispatch_d(const DecodeArgs& a, int D, int bs, int G, hipStream_t st) {
+  switch (D) {
+    case 64: return dispatch_bs<DT, 64>(a, bs, G, st);
+    case 128: return dispatch_bs<DT, 128>(a, bs, G, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline int32_t num_partitions(int32_t max_ctx, int32_t part_tokens) {
+  return part_tokens > 0 ? (max_ctx + part_tokens - 1) / part_tokens : 1;
+}
+
+}  // namespace pa
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
+                                            int32_t max_context_len, int32_t partition_tokens) {
+  if (S <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0 || partition_tokens <= 0) return 0;
+  const int32_t pmax = pa::num_partitions(max_context_len, partition_tokens);
+  if (pmax <= 1) return 0;
+  const size_t n = static_cast<size_t>(S) * Hq * pmax;
+  return 2 * pa::align256(n * sizeof(float)) + pa::align256(n * D * sizeof(float));
+}
+
+extern "C" int pa_decode_attention(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t S, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                                   int32_t max_context_len, float scale,
+                                   int32_t partition_tokens, void* workspace,
+                                   size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (pa::elem_bytes(dtype) == 0) return PA_ERR_INVALID;
+  if (S < 0 || Hq < 1 || Hkv < 1 || D < 1 || bs < 1 || NB < 1 || MB < 1) return PA_ERR_INVALID;
+  if (max_context_len < 1 || partition_tokens < 0) return PA_ERR_INVALID;
+  if (partition_tokens > 0 && partition_tokens % bs) return PA_ERR_INVALID;
+  if (Hq % Hkv) return PA_ERR_INVALID;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID;
+  if (S == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID;
+  if (!pa::aligned16(out) || !pa::aligned16(query) || !pa::aligned16(key_cache) ||
+      !pa::aligned16(value_cache))
+    return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return PA_ERR_INVALID;
+  const int G = Hq / Hkv;
+  if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
+  if (bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  const int32_t eff_ctx = static_cast<int32_t>(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(MB) * bs));
+  const int32_t pmax = pa::num_partitions(eff_ctx, partition_tokens);
+  if (S > 65535 || pmax > 65535) return PA_ERR_UNSUPPORTED;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.NB = NB;
+  a.MB = MB;
+  a.max_ctx = eff_ctx;
+  a.part_tokens = pmax > 1 ? partition_tokens : 0;
+  a.pmax = pmax;
+  a.qscale = scale * pa::kLog2e;
+  if (pmax > 1) {
+    const size_t need = pa_decode_workspace_bytes(S, Hq, D, eff_ctx, partition_tokens);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return PA_ERR_WORKSPACE;
+    const size_t n = static_cast<size_t>(S) * Hq * pmax;
+    char* base = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(base);
+    a.ws_l = reinterpret_cast<float*>(base + pa::align256(n * sizeof(float)));
+    a.ws_o = reinterpret_cast<float*>(base + 2 * pa::align256(n * sizeof(float)));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case PA_F32: return pa::dispatch_d<PA_F32>(a, D, bs, G, st);
+    case PA_F16: return pa::dispatch_d<PA_F16>(a, D, bs, G, st);
+    case PA_BF16: return pa::dispatch_d<PA_BF16>(a, D, bs, G, st);
+    default: return PA_ERR_INVALID;
+  }
+}

@@ -96,6 +96,7 @@ class DecodeWorkload:
     partition_tokens: int
     context_lens: np.ndarray     # int32 [S]
     block_tables: np.ndarray     # int32 [S, MB], -1 past the sequence's blocks
+    block_order: np.ndarray      # int32 [NB] the permutation the tables were cut from
     q: torch.Tensor              # [S, Hq, D]
     key_cache: torch.Tensor      # [NB, Hkv, bs, D] pre-step
     value_cache: torch.Tensor    # [NB, Hkv, bs, D] pre-step
@@ -116,9 +117,10 @@ class DecodeWorkload:
 
 
 def paged_tables(rng: np.random.Generator, lens: np.ndarray, bs: int, NB: int,
-                 MB: Optional[int] = None) -> np.ndarray:
+                 MB: Optional[int] = None):
     """Assign each sequence ceil(ctx/bs) physical blocks, consecutively from one
-    random permutation of the pool (so neighbours in a table are scattered)."""
+    random permutation of the pool (so neighbours in a table are scattered).
+    Returns (tables, permutation)."""
     nblk = (lens.astype(np.int64) + bs - 1) // bs
     if int(nblk.sum()) > NB:
         raise ValueError(f"pool of {NB} blocks cannot hold {int(nblk.sum())}")
@@ -129,7 +131,7 @@ def paged_tables(rng: np.random.Generator, lens: np.ndarray, bs: int, NB: int,
     for s, n in enumerate(nblk):
         tables[s, :n] = perm[off:off + n]
         off += n
-    return tables
+    return tables, perm
 
 
 def filled_mask(tables: np.ndarray, filled: np.ndarray, bs: int, NB: int) -> np.ndarray:
@@ -154,7 +156,7 @@ def make_decode(name: str, seed: int = 0, device="cpu", **over) -> DecodeWorkloa
     NB = cfg["NB"] if cfg.get("NB") else cfg["pool_tokens"] // bs
     rng = np.random.default_rng(seed)
     lens = draw_lengths(rng, cfg["lengths"], S)
-    tables = paged_tables(rng, lens, bs, NB, cfg.get("MB"))
+    tables, perm = paged_tables(rng, lens, bs, NB, cfg.get("MB"))
     mask = filled_mask(tables, np.maximum(lens.astype(np.int64) - 1, 0), bs, NB)
     gen = _generator(seed, device)
     dt = cfg["dtype"]
@@ -172,7 +174,7 @@ def make_decode(name: str, seed: int = 0, device="cpu", **over) -> DecodeWorkloa
         name=name, seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
         scale=float(np.float32(1.0 / np.sqrt(D))),
         partition_tokens=int(cfg.get("partition_tokens", 0)),
-        context_lens=lens, block_tables=tables, q=q,
+        context_lens=lens, block_tables=tables, block_order=perm, q=q,
         key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
 
 
