@@ -277,8 +277,6 @@ def main():
     }
     if not args.no_probe:
         line["hbm_probe"] = hbm_probe(torch)
-        best = max(line["hbm_probe"].values())
-        line["roofline"]["frac_of_probe"] = achieved / best
     if args.calibrate_copy:
         calibrate_copy(torch)
     if not args.no_cpu_baseline:

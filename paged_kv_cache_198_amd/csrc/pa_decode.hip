@@ -23,11 +23,13 @@
 // (quad_perm, row_half_mirror, row_mirror; ds_swizzle for 32 lanes), which
 // leaves the full dot product in every lane of the row.
 //
-// Block-table entries for the workgroup's range are staged in LDS once per
-// chunk of kTableChunk blocks; K/V rows go straight from HBM to registers
-// (each byte is consumed by exactly one lane, so an LDS hop would add traffic
-// without reuse).  Tokens past the context are never loaded: their loads are
-// predicated off and their weights are exactly zero.
+// A wavefront's token rows never straddle a block, so the block-table entry
+// of each row group is wave-uniform: it is read with a scalar load and folded
+// into the scalar base of the vector loads.  K/V rows go straight from HBM to
+// registers (each byte is consumed by exactly one lane, so an LDS hop would
+// add traffic without reuse).  Tiles wholly inside the context load without
+// predication; in the last tile, tokens past the context are never loaded
+// and their weights are exactly zero.
 //
 // Split context.  With partition_tokens > 0 each partition writes
 // (m, l, unnormalised acc) in float32 to the workspace and reduce_kernel
@@ -43,8 +45,32 @@
 namespace pa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kWaves = 4;
-constexpr int kTableChunk = 1024;
+// Tuning (measured on the 13B-shaped batch, see profiles/): 8 waves per
+// workgroup and 8 rows per lane per tile; non-temporal K/V loads raise the
+// achieved read bandwidth by about 12%.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 8
+#endif
+#ifndef PA_DECODE_ROWS
+#define PA_DECODE_ROWS 8
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+constexpr int kWaves = PA_DECODE_WAVES;   // wavefronts per workgroup
+constexpr int kRows = PA_DECODE_ROWS;     // token rows per lane per tile (G < 4)
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// K/V rows are read exactly once: optionally mark the loads non-temporal.
+__device__ __forceinline__ uint4 load_kv(const void* p) {
+#if PA_DECODE_NT
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
 
 template <int DT> struct KV;
 template <> struct KV<PA_F32> { using T = float; static constexpr int kBytes = 4; };
@@ -144,19 +170,18 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   constexpr int VEC = 16 / EB;           // elements per lane chunk
   constexpr int RL = D * EB / 16;        // lanes per token row
   constexpr int RPW = 64 / RL;           // token rows per wave load
-  constexpr int NL = (G >= 4) ? 4 : 8;   // rows per lane per tile
+  constexpr int NL = (G >= 4) ? 4 : kRows;  // rows per lane per tile
   constexpr int TILE = NL * RPW;         // tokens per wave per tile
   constexpr float kNegInf = -INFINITY;
 
-  __shared__ int32_t tbl[kTableChunk];
   __shared__ float red_acc[kWaves][G][D];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
 
   const int g = blockIdx.x;
-  const int s = blockIdx.y;
   const int p = blockIdx.z;
   const int tid = threadIdx.x;
+  const int s = blockIdx.y;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane / RL;
@@ -189,81 +214,96 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < VEC; ++e) acc[gi][e] = 0.f;
   }
 
+  // Row group j of a tile starting at t0 holds tokens t0 + j*RPW + [0, RPW):
+  // t0 is a multiple of RPW and RPW divides bs, so those RPW tokens share one
+  // block and the block number is the same for the whole wavefront.  It is
+  // read with a scalar load and folded into the scalar base address; the only
+  // per-lane address term is the lane's row and 16-byte column.
   const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.MB;
-  const size_t block_stride = static_cast<size_t>(a.Hkv) * BS * D;
-  const T* kb = static_cast<const T*>(a.key_cache) + static_cast<size_t>(g) * BS * D + c * VEC;
-  const T* vb = static_cast<const T*>(a.value_cache) + static_cast<size_t>(g) * BS * D + c * VEC;
+  const size_t bstride = static_cast<size_t>(a.Hkv) * BS * D * EB;  // bytes per block
+  const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * D * EB;
+  const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * D * EB;
+  const uint32_t lane_off = static_cast<uint32_t>((r * D + c * VEC) * EB);
+  const int last_lb = end > 0 ? (end - 1) / BS : 0;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
 
-  for (int cs = start; cs < end; cs += kTableChunk * BS) {
-    const int ce = min(end, cs + kTableChunk * BS);
-    const int b0 = cs / BS;
-    const int nb = (ce - 1) / BS - b0 + 1;
-    __syncthreads();
-    for (int i = tid; i < nb; i += kWaves * 64) tbl[i] = trow[b0 + i];
-    __syncthreads();
-
-    for (int t0 = cs + w * TILE; t0 < ce; t0 += kWaves * TILE) {
-      uint4 kr[NL], vr[NL];
-      bool ok[NL];
+  for (int t0 = start + wv * TILE; t0 < end; t0 += kWaves * TILE) {
+    size_t off[NL];
+    bool bok[NL];
+    bool whole = t0 + TILE <= end;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int tj = t0 + j * RPW;
+      const int blk = trow[min(tj / BS, last_lb)];
+      bok[j] = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
+      whole = whole && bok[j];
+      off[j] = static_cast<size_t>(blk) * bstride + static_cast<size_t>(tj % BS) * (D * EB);
+    }
+    uint4 kr[NL], vr[NL];
+    bool ok[NL];
+    if (whole) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int t = t0 + j * RPW + r;
-        const int bi = min(t / BS - b0, nb - 1);
-        const int blk = tbl[bi];
-        ok[j] = t < ce && static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
-        const size_t off = static_cast<size_t>(blk) * block_stride + static_cast<size_t>(t % BS) * D;
+        kr[j] = load_kv(kb + off[j] + lane_off);
+        vr[j] = load_kv(vb + off[j] + lane_off);
+        ok[j] = true;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        ok[j] = bok[j] && t0 + j * RPW + r < end;
         uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
         if (ok[j]) {
-          kv = *reinterpret_cast<const uint4*>(kb + off);
-          vv = *reinterpret_cast<const uint4*>(vb + off);
+          kv = load_kv(kb + off[j] + lane_off);
+          vv = load_kv(vb + off[j] + lane_off);
         }
         kr[j] = kv;
         vr[j] = vv;
       }
+    }
 
-      // logits (log2 domain) for the NL rows of this lane, every head
-      float sc[NL][G];
+    // logits (log2 domain) for the NL rows of this lane, every head
+    float sc[NL][G];
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        float kf[VEC];
-        widen16<DT>(kr[j], kf);
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) d = fmaf(qf[gi][e], kf[e], d);
-          sc[j][gi] = row_sum<RL>(d);
-        }
-      }
-
-      // online softmax: rescale once per tile, then accumulate
-      float pw[NL][G];
+    for (int j = 0; j < NL; ++j) {
+      float kf[VEC];
+      widen16<DT>(kr[j], kf);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
-        float mt = kNegInf;
+        float d = 0.f;
 #pragma unroll
-        for (int j = 0; j < NL; ++j) mt = ok[j] ? fmaxf(mt, sc[j][gi]) : mt;
-        const float mn = fmaxf(m[gi], mt);
-        const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[gi] - mn);
-        l[gi] *= alpha;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[gi][e] *= alpha;
-        m[gi] = mn;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-          pw[j][gi] = ok[j] ? fast_exp2(sc[j][gi] - mn) : 0.f;
-          l[gi] += pw[j][gi];
-        }
+        for (int e = 0; e < VEC; ++e) d = fmaf(qf[gi][e], kf[e], d);
+        sc[j][gi] = row_sum<RL>(d);
       }
+    }
+
+    // online softmax: rescale once per tile, then accumulate
+    float pw[NL][G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      float mt = kNegInf;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) mt = ok[j] ? fmaxf(mt, sc[j][gi]) : mt;
+      const float mn = fmaxf(m[gi], mt);
+      const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[gi] - mn);
+      l[gi] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[gi][e] *= alpha;
+      m[gi] = mn;
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        float vf[VEC];
-        widen16<DT>(vr[j], vf);
-#pragma unroll
-        for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[gi][e] = fmaf(pw[j][gi], vf[e], acc[gi][e]);
+        pw[j][gi] = ok[j] ? fast_exp2(sc[j][gi] - mn) : 0.f;
+        l[gi] += pw[j][gi];
       }
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      float vf[VEC];
+      widen16<DT>(vr[j], vf);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[gi][e] = fmaf(pw[j][gi], vf[e], acc[gi][e]);
     }
   }
 
