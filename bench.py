@@ -32,7 +32,17 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama13b_bs16.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_198_amd", "csrc", "pa_decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_198_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_device.h")]
+
+
+def decode_source_sha() -> str:
+    """Hash of the sources the VALU decode kernel is built from."""
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -40,6 +50,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama13b",
+                    choices=["llama13b", "llama7b", "long_gqa", "tiny"],
+                    help="decode workload to time (default: the 13B-shaped batch)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition tokens (0 = single pass, -1 = library default for the shape)")
@@ -52,17 +65,22 @@ def parse():
     return ap.parse_args()
 
 
-def default_partition(bs: int) -> int:
-    return 0
+def default_partition(workload: str) -> int:
+    """Partition size per workload: the long-context batch has only S*Hkv = 64
+    (sequence, KV head) pairs, so it is split into 512-token partitions to
+    fill the chip; the others run in one pass."""
+    from paged_kv_cache_198_amd import synth
+    return synth.CONFIGS[workload]["partition_tokens"]
 
 
 class Step:
     """Device state of one decode step, built once."""
 
-    def __init__(self, pa, synth, torch, bs, seed, partition):
+    def __init__(self, pa, synth, torch, bs, seed, partition, workload="llama13b"):
         self.torch = torch
         self.pa = pa
-        w = synth.make_decode("llama13b", seed=seed, device="cuda", bs=bs)
+        over = {"bs": bs} if workload == "llama13b" else {}
+        w = synth.make_decode(workload, seed=seed, device="cuda", **over)
         self.w = w
         alloc = pa.Allocator(w.NB, w.bs, init_order=w.block_order)
         step = np.empty(w.S, dtype=np.int64)
@@ -75,7 +93,7 @@ class Step:
         self.tables = torch.from_numpy(tables).cuda()
         self.lens = torch.from_numpy(lens).cuda()
         self.max_ctx = int(lens.max())
-        self.part = default_partition(bs) if partition < 0 else partition
+        self.part = default_partition(workload) if partition < 0 else partition
         self.out = torch.empty(w.S, w.Hq, w.D, dtype=w.q.dtype, device="cuda")
         self.ws = pa.make_workspace(w.S, w.Hq, w.D, self.max_ctx, self.part)
         self.kv_bytes = int(np.sum(lens.astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
@@ -114,6 +132,18 @@ class Step:
         return step_ms, attn_ms, wall
 
 
+def describe(name, w) -> str:
+    from paged_kv_cache_198_amd import synth
+    law = synth.CONFIGS[name]["lengths"]
+    lens = (f"lognormal(median {law[1]}, sigma {law[2]}) in [{law[3]}, {law[4]}]"
+            if law[0] == "lognormal" else f"uniform in [{law[1]}, {law[2]}]")
+    title = {"llama13b": "LLaMA-13B-shaped decode layer", "llama7b": "LLaMA-7B-shaped decode layer",
+             "long_gqa": "long-context GQA decode (one GPU's share of a 70B-shaped layer)",
+             "tiny": "tiny paged decode"}[name]
+    return (f"{title}: S={w.S}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, {w.dtype} KV, block_size {w.bs}, "
+            f"ctx {lens}, {w.NB}-block pool shuffled, 1 new token per sequence")
+
+
 def traffic_bytes():
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
@@ -121,8 +151,7 @@ def traffic_bytes():
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    sha = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-    if t.get("kernel_source_sha256") != sha:
+    if t.get("kernel_source_sha256") != decode_source_sha():
         return None
     return float(t["bytes_per_launch"])
 
@@ -214,15 +243,15 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     pa.lib()
-    print(f"[bench] building workload llama13b bs={args.bs}", file=sys.stderr, flush=True)
-    st = Step(pa, synth, torch, args.bs, args.seed, args.partition)
+    print(f"[bench] building workload {args.workload} bs={args.bs}", file=sys.stderr, flush=True)
+    st = Step(pa, synth, torch, args.bs, args.seed, args.partition, args.workload)
     w = st.w
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
     step_ms, attn_ms, wall = st.run(args.steps, args.warmup)
 
     sweep = {}
-    if not args.no_sweep:
+    if not args.no_sweep and args.workload == "llama13b":
         for bs in (8, 16, 32):
             if bs == args.bs:
                 continue
@@ -253,10 +282,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q/K/V, lognormal context lengths)",
         "config": {
-            "workload": f"LLaMA-13B-shaped decode layer: S={w.S}, Hq=Hkv={w.Hkv}, D={w.D}, "
-                        f"{w.dtype} KV, block_size {w.bs}, ctx lognormal(700, 0.5) in "
-                        f"[1, 2048], {w.NB}-block pool shuffled, 1 new token per sequence",
-            "S": w.S, "heads": w.Hq, "head_dim": w.D, "block_size": w.bs,
+            "workload": describe(args.workload, w),
+            "S": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.bs,
             "tokens": int(np.sum(w.context_lens)), "kv_bytes": st.kv_bytes,
             "partition_tokens": st.part, "seed": args.seed,
         },
@@ -268,7 +295,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_bytes(),
+            "traffic": traffic_bytes() if (args.workload == "llama13b" and args.bs == 16) else None,
             "kernel": "pa::decode_kernel" + (" + reduce_kernel" if st.part else ""),
             "algorithmic_bytes_per_launch": st.kv_bytes,
         },

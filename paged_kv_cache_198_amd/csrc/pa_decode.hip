@@ -40,128 +40,13 @@
 #include <cmath>
 
 #include "pa.h"
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-// Tuning (measured on the 13B-shaped batch, see profiles/): 8 waves per
-// workgroup and 8 rows per lane per tile; non-temporal K/V loads raise the
-// achieved read bandwidth by about 12%.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 8
-#endif
-#ifndef PA_DECODE_ROWS
-#define PA_DECODE_ROWS 8
-#endif
-#ifndef PA_DECODE_NT
-#define PA_DECODE_NT 1
-#endif
 constexpr int kWaves = PA_DECODE_WAVES;   // wavefronts per workgroup
 constexpr int kRows = PA_DECODE_ROWS;     // token rows per lane per tile (G < 4)
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// K/V rows are read exactly once: optionally mark the loads non-temporal.
-__device__ __forceinline__ uint4 load_kv(const void* p) {
-#if PA_DECODE_NT
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
-}
-
-template <int DT> struct KV;
-template <> struct KV<PA_F32> { using T = float; static constexpr int kBytes = 4; };
-template <> struct KV<PA_F16> { using T = _Float16; static constexpr int kBytes = 2; };
-template <> struct KV<PA_BF16> { using T = uint16_t; static constexpr int kBytes = 2; };
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-// 16 bytes of stored elements -> float32.
-template <int DT>
-__device__ __forceinline__ void widen16(const uint4& c, float* f) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  if constexpr (DT == PA_F32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, w[i]);
-  } else if constexpr (DT == PA_F16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const half2_t h = __builtin_bit_cast(half2_t, w[i]);
-      f[2 * i] = static_cast<float>(h.x);
-      f[2 * i + 1] = static_cast<float>(h.y);
-    }
-  } else {
-    // bfloat16 is the upper half of a float32.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-      f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-    }
-  }
-}
-
-// float32 -> stored element, round to nearest even.
-template <int DT>
-__device__ __forceinline__ typename KV<DT>::T narrow(float x) {
-  if constexpr (DT == PA_F32) {
-    return x;
-  } else if constexpr (DT == PA_F16) {
-    return static_cast<_Float16>(x);
-  } else {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-  }
-}
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
-}
-
-// Sum over the RL consecutive lanes of a token row; every lane of the row
-// ends with the same value (each step adds a value and its partner's, and
-// float addition is commutative).
-template <int RL>
-__device__ __forceinline__ float row_sum(float x) {
-  static_assert(RL == 8 || RL == 16 || RL == 32, "row width");
-  x += dpp<0xb1>(x);   // quad_perm [1,0,3,2]
-  x += dpp<0x4e>(x);   // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);  // row_half_mirror: quads 0<->1 of each 8
-  if constexpr (RL >= 16) x += dpp<0x140>(x);  // row_mirror: halves of a 16-lane row
-  if constexpr (RL >= 32)                      // lane ^ 16 inside each 32
-    x += __builtin_bit_cast(float,
-                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
-  return x;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-struct DecodeArgs {
-  void* out;
-  const void* q;
-  const void* key_cache;
-  const void* value_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  float* ws_m;
-  float* ws_l;
-  float* ws_o;
-  int32_t S, Hq, Hkv, NB, MB, max_ctx;
-  int32_t part_tokens;  // 0: one pass over the whole context
-  int32_t pmax;         // partitions per sequence in the grid / workspace
-  float qscale;         // scale * log2(e)
-};
-
-__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s, int bs) {
-  const int c = a.context_lens[s];
-  return max(0, min(c, min(a.max_ctx, a.MB * bs)));
-}
 
 template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
@@ -400,11 +285,30 @@ int launch_decode(const DecodeArgs& a, hipStream_t st) {
                      dim3(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
                           static_cast<uint32_t>(a.pmax)),
                      dim3(kWaves * 64), 0, st, a);
-  if (a.part_tokens > 0 && a.pmax > 1)
-    hipLaunchKernelGGL((reduce_kernel<DT, D, BS>),
-                       dim3(static_cast<uint32_t>(a.Hq), static_cast<uint32_t>(a.S)), dim3(D), 0,
-                       st, a);
   return launch_status();
+}
+
+template <int DT, int D, int BS>
+int launch_reduce(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((reduce_kernel<DT, D, BS>),
+                     dim3(static_cast<uint32_t>(a.Hq), static_cast<uint32_t>(a.S)), dim3(D), 0,
+                     st, a);
+  return launch_status();
+}
+
+template <int DT, int D>
+int dispatch_reduce(const DecodeArgs& a, int bs, hipStream_t st) {
+  switch (bs) {
+    case 8: return launch_reduce<DT, D, 8>(a, st);
+    case 16: return launch_reduce<DT, D, 16>(a, st);
+    case 32: return launch_reduce<DT, D, 32>(a, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+template <int DT>
+int dispatch_reduce_d(const DecodeArgs& a, int D, int bs, hipStream_t st) {
+  return D == 64 ? dispatch_reduce<DT, 64>(a, bs, st) : dispatch_reduce<DT, 128>(a, bs, st);
 }
 
 template <int DT, int D, int BS>
@@ -512,10 +416,24 @@ extern "C" int pa_decode_attention(void* out, const void* query, const void* key
     a.ws_o = reinterpret_cast<float*>(base + 2 * pa::align256(n * sizeof(float)));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // Grouped heads that fill a matrix-core tile go to the MFMA kernel; every
+  // other shape runs the vector-ALU kernel.
+  const bool mfma = (dtype == PA_BF16 || dtype == PA_F16) && D == 128 && G == 8 &&
+                    a.part_tokens % 32 == 0;
+  int rc;
+  if (mfma) {
+    rc = pa::launch_decode_gqa_mfma(a, dtype, bs, st);
+  } else {
+    switch (dtype) {
+      case PA_F32: rc = pa::dispatch_d<PA_F32>(a, D, bs, G, st); break;
+      case PA_F16: rc = pa::dispatch_d<PA_F16>(a, D, bs, G, st); break;
+      default: rc = pa::dispatch_d<PA_BF16>(a, D, bs, G, st); break;
+    }
+  }
+  if (rc != PA_OK || pmax <= 1) return rc;
   switch (dtype) {
-    case PA_F32: return pa::dispatch_d<PA_F32>(a, D, bs, G, st);
-    case PA_F16: return pa::dispatch_d<PA_F16>(a, D, bs, G, st);
-    case PA_BF16: return pa::dispatch_d<PA_BF16>(a, D, bs, G, st);
-    default: return PA_ERR_INVALID;
+    case PA_F32: return pa::dispatch_reduce_d<PA_F32>(a, D, bs, st);
+    case PA_F16: return pa::dispatch_reduce_d<PA_F16>(a, D, bs, st);
+    default: return pa::dispatch_reduce_d<PA_BF16>(a, D, bs, st);
   }
 }

@@ -1,0 +1,380 @@
+// Paged decode attention for grouped-query heads on the gfx950 matrix cores.
+//
+// "PagedAttention: the KV cache was the bottleneck all along", section
+// "Virtual memory for attention": keys and values are gathered from scattered
+// fixed-size blocks through the sequence's block table.  When G = Hq/Hkv
+// query heads share one KV head, the two products of a decode step are dense
+// contractions over a tile of T tokens: S = Q_g K^T ([G x D] . [D x T]) and
+// O = P V ([G x T] . [T x D]).  This kernel runs both on
+// v_mfma_f32_16x16x32_{bf16,f16} (G = 8 padded to the 16-wide tile, D = 128);
+// the step stays bound by HBM, the matrix cores only take the arithmetic off
+// the vector ALUs.
+//
+// Per wavefront and 32-token tile (t0 a multiple of 32, so the tile starts on
+// a block boundary for bs in {8, 16, 32}):
+//   * K and V rows are loaded coalesced (16 lanes x 16 B per 256-byte row)
+//     with raw buffer loads, one resource per block; rows past the context
+//     load zero without touching memory, so no load sits behind a branch.
+//   * S^T = K . Q^T, as two 16-token MFMA tiles x 4 k-steps of 32 dims:
+//     A = K through the wavefront's LDS tile (lane l: token l%16, dims
+//     8*(l/16) + 32kk .. +8, one 16-byte read), B = Q^T kept in registers
+//     (lane l: head l%16, zero for the padding heads).  Lane l then holds the
+//     scores of tokens 16u + 4(l/16) + i (i = 0..3) for head l%16.
+//   * online softmax per head (max across the 4 lane groups of a head with
+//     two shuffles; the running sum stays per lane and is added up at the
+//     end); the reference max moves only when it grows by more than 2^8, so
+//     the accumulators are rarely rescaled.
+//   * O^T += V^T . P^T: B = P^T is already where the scores left it (lane l:
+//     head l%16, the 8 tokens 4(l/16)+i and 16+4(l/16)+i), A = V^T comes from
+//     the same LDS tile, now holding the V rows (rows padded to 272 bytes, so
+//     the 4 lane groups read disjoint banks).  The output rows of O^T are dims
+//     and its columns heads, so lane l holds head l%16: the per-head rescale
+//     factor never leaves the lane.
+// Probabilities enter the second product rounded to the KV type; the running
+// sum adds the same rounded values, so numerator and denominator agree.
+#include <hip/hip_runtime.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kMWaves = 4;                 // wavefronts per workgroup
+constexpr int kMTile = 32;                 // tokens per wavefront per tile
+constexpr int kMD = 128;                   // head dim
+constexpr int kMG = 8;                     // query heads per KV head
+constexpr int kVRow = kMD * 2 + 16;        // padded LDS row of one V token (bytes)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mma(const u16x8_t& a, const u16x8_t& b, const f32x4_t& c) {
+  if constexpr (DT == PA_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// float -> 16-bit pattern of the KV type (round to nearest even) and back.
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits(float x) {
+  if constexpr (DT == PA_BF16) return narrow<PA_BF16>(x);
+  else return __builtin_bit_cast(uint16_t, narrow<PA_F16>(x));
+}
+template <int DT>
+__device__ __forceinline__ float from_bits(uint16_t b) {
+  if constexpr (DT == PA_BF16) return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+__device__ __forceinline__ u16x8_t as_u16x8(const uint4& v) {
+  return __builtin_bit_cast(u16x8_t, v);
+}
+
+// bok[i] for a lane-dependent i < N (wave-uniform entries)
+template <int N>
+__device__ __forceinline__ bool pick_ok(const bool (&v)[N], int i) {
+  bool r = v[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = (i == k) ? v[k] : r;
+  return r;
+}
+
+// The per-wavefront LDS tile is written and read by the same wavefront,
+// whose LDS operations the hardware performs in order; this only stops the
+// compiler from moving LDS accesses across the point.
+__device__ __forceinline__ void lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // past every resource's end
+
+// Raw buffer resource over [base, base + bytes): stride 0, the gfx9 data
+// format word.  Loads at offsets >= bytes return zero and access nothing.
+__device__ __forceinline__ rsrc_t make_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16-byte load; K/V are read once, so the non-temporal bit is set (cache
+// policy operand: sc0 = 1, nt = 2, sc1 = 16).
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0,
+                                                          PA_DECODE_NT ? 2 : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr float kLazy = 8.f;               // lazy-rescale threshold (log2 units)
+
+// Registers of one tile in flight: K and V rows (token t0 + 4j + q, 16-byte
+// column n), block flags.
+template <int NBK>
+struct TileRegs {
+  uint4 kr[8];
+  uint4 vr[8];
+  bool bok[NBK];
+};
+
+template <int DT, int BS>
+__global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  using T = typename KV<DT>::T;
+  constexpr float kNegInf = -INFINITY;
+  constexpr int NBK = kMTile / BS;         // blocks per tile (bs divides 32)
+  static_assert(kMTile % BS == 0 && BS >= 4, "block size");
+  using Tile = TileRegs<NBK>;
+
+  // Per-wavefront K/V tiles during the loop; the same bytes hold the
+  // cross-wavefront merge afterwards.
+  struct Merge {
+    float o[kMWaves][kMG][kMD];
+    float m[kMWaves][kMG];
+    float l[kMWaves][kMG];
+  };
+  constexpr int kTileBytes = kMWaves * kMTile * kVRow;
+  constexpr int kSmem = kTileBytes > static_cast<int>(sizeof(Merge)) ? kTileBytes : sizeof(Merge);
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  Merge& red = *reinterpret_cast<Merge*>(smem);
+
+  const int g = blockIdx.x;
+  const int s = blockIdx.y;
+  const int p = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 15;                 // head (scores, output) / token row (K) / d col
+  const int q = lane >> 4;                 // lane group
+
+  const int ctx = clamp_ctx(a, s, BS);
+  const int PT = a.part_tokens > 0 ? a.part_tokens : max(ctx, 1);
+  const int nparts = max(1, (ctx + PT - 1) / PT);
+  if (p >= nparts) return;
+  const int start = p * PT;
+  const int end = min(ctx, start + PT);
+
+  // B operand of S^T = K Q^T: lane (n, q) holds q[head n][32kk + 8q .. +8].
+  u16x8_t qt[4];
+  {
+    const T* qb = static_cast<const T*>(a.q) + (static_cast<size_t>(s) * a.Hq + g * kMG) * kMD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < kMG) v = *reinterpret_cast<const uint4*>(qb + n * kMD + 32 * kk + 8 * q);
+      qt[kk] = as_u16x8(v);
+    }
+  }
+
+  float m_run = kNegInf;                   // reference max of head n (log2 domain)
+  float l_run = 0.f;                       // this lane's share of head n's sum
+  f32x4_t o[8];                            // O^T tile dt: dims 16dt + 4q + i, head n
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.MB;
+  const size_t bstride = static_cast<size_t>(a.Hkv) * BS * kMD * 2;
+  const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kMD * 2;
+  const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kMD * 2;
+  const int last_lb = end > 0 ? (end - 1) / BS : 0;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  char* vt = smem + w * (kMTile * kVRow);
+
+  // Issue every load of the tile at t0.  Each block's head tile is one buffer
+  // resource; a row past the context, or in a block outside the pool, gets
+  // an offset past the resource's end and loads zero without touching
+  // memory, so no load sits behind a branch.
+  auto issue = [&](int t0, Tile& tl) {
+    int blk[NBK];
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      blk[b] = trow[min(t0 / BS + b, last_lb)];
+      tl.bok[b] = static_cast<unsigned>(blk[b]) < static_cast<unsigned>(a.NB);
+    }
+    rsrc_t kres[NBK], vres[NBK];
+#pragma unroll
+    for (int b = 0; b < NBK; ++b) {
+      const size_t off = tl.bok[b] ? static_cast<size_t>(blk[b]) * bstride : 0;
+      const uint32_t bytes = tl.bok[b] ? static_cast<uint32_t>(BS * kMD * 2) : 0u;
+      kres[b] = make_rsrc(kb + off, bytes);
+      vres[b] = make_rsrc(vb + off, bytes);
+    }
+    // K and V rows, coalesced: 16 lanes x 16 B per 256-byte row, four rows
+    // (tokens t0 + 4j + q) per instruction.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rel = 4 * j + q;
+      const uint32_t voff =
+          t0 + rel < end ? static_cast<uint32_t>((rel % BS) * (kMD * 2) + 16 * n) : kOutOfRange;
+      tl.kr[j] = buffer_load16(kres[(4 * j) / BS], voff);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rel = 4 * j + q;
+      const uint32_t voff =
+          t0 + rel < end ? static_cast<uint32_t>((rel % BS) * (kMD * 2) + 16 * n) : kOutOfRange;
+      tl.vr[j] = buffer_load16(vres[(4 * j) / BS], voff);
+    }
+  };
+
+  // Scores, online softmax and the V product for the tile at t0 (< end).
+  auto consume = [&](int t0, const Tile& tl) {
+    // K rows through LDS into the A-operand layout: lane (n, q) of sub-tile
+    // u takes 16 bytes of token 16u + n at dims 32kk + 8q.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.kr[j];
+    lds_order();
+    f32x4_t sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4*>(vt + (16 * u + n) * kVRow + 64 * kk + 16 * q);
+        sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
+      }
+    }
+    lds_order();
+    float sv[8];
+    float mt = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rel = 16 * u + 4 * q + i;
+        const bool ok = t0 + rel < end && pick_ok(tl.bok, rel / BS);
+        const float x = ok ? sc[u][i] * a.qscale : kNegInf;
+        sv[4 * u + i] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // Lazy rescale: the reference max moves only when the tile's max exceeds
+    // it by more than kLazy (log2 units), so weights stay <= 2^kLazy and the
+    // accumulators are rarely touched.
+    const bool bump = mt > m_run + kLazy;
+    const float mn = bump ? mt : m_run;
+    if (__any(bump)) {
+      const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    m_run = mn;
+    u16x8_t pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+      const uint16_t bits = to_bits<DT>(pv);
+      pb[jj] = bits;
+      psum += from_bits<DT>(bits);
+    }
+    l_run += psum;
+
+    // V rows to LDS (over the K rows, whose reads are done), then read back
+    // transposed.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
+    lds_order();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      u16x8_t va;
+      const char* col = vt + (16 * dt + n) * 2;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int row = (jj < 4) ? 4 * q + jj : 16 + 4 * q + (jj - 4);
+        va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kVRow);
+      }
+      o[dt] = mma<DT>(va, pb, o[dt]);
+    }
+    lds_order();                           // the next tile rewrites these rows
+  };
+
+  constexpr int kStride = kMWaves * kMTile;
+  for (int t0 = start + wv * kMTile; t0 < end; t0 += kStride) {
+    Tile ta;
+    issue(t0, ta);
+    consume(t0, ta);
+  }
+  __syncthreads();                         // every wavefront is done with its tile
+
+  // head n's sum over the four lane groups
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (n < kMG) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red.o[w][n][16 * dt + 4 * q + i] = o[dt][i];
+    if (q == 0) {
+      red.m[w][n] = m_run;
+      red.l[w][n] = l_run;
+    }
+  }
+  __syncthreads();
+
+  for (int i = tid; i < kMG * kMD; i += kMWaves * 64) {
+    const int gi = i / kMD;
+    const int d = i - gi * kMD;
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kMWaves; ++v) M = fmaxf(M, red.m[v][gi]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int v = 0; v < kMWaves; ++v) {
+      const float mv = red.m[v][gi];
+      const float sw = (mv == kNegInf) ? 0.f : fast_exp2(mv - M);
+      num = fmaf(red.o[v][gi][d], sw, num);
+      den = fmaf(red.l[v][gi], sw, den);
+    }
+    const int h = g * kMG + gi;
+    if (nparts == 1) {
+      static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * kMD + d] =
+          narrow<DT>(den > 0.f ? num / den : 0.f);
+    } else {
+      const size_t idx = (static_cast<size_t>(s) * a.Hq + h) * a.pmax + p;
+      a.ws_o[idx * kMD + d] = num;
+      if (d == 0) {
+        a.ws_m[idx] = M;
+        a.ws_l[idx] = den;
+      }
+    }
+  }
+}
+
+template <int DT>
+int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
+  const dim3 grid(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
+                  static_cast<uint32_t>(a.pmax));
+  switch (bs) {
+    case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    default: return PA_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+int launch_decode_gqa_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st) {
+  switch (dtype) {
+    case PA_BF16: return launch_bs<PA_BF16>(a, bs, st);
+    case PA_F16: return launch_bs<PA_F16>(a, bs, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace pa

@@ -471,3 +471,31 @@ def test_shared_prefix(prompt_len, full):
     err = float(np.max(np.abs(got - ref)))
     note(f"  copies {copies}, max abs err {err:.3e}")
     assert err <= TOL[sc.dtype]
+
+
+# ---------------------------------------------------------------------------
+# grouped heads on the matrix cores (G = 8, D = 128, bf16 / f16): block sizes,
+# partitions (multiples of 32 take the MFMA kernel, others the vector-ALU one)
+# and lengths around tile, block and partition edges
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,bs,part", [("bf16", 8, 512), ("bf16", 32, 0), ("f16", 16, 512),
+                                           ("f16", 16, 0), ("bf16", 16, 96), ("bf16", 16, 48),
+                                           ("f16", 8, 64)])
+def test_gqa_matrix_core(dtype, bs, part):
+    w = synth.make_decode("long_gqa", device=DEV, S=4, NB=2048, bs=bs, dtype=dtype,
+                          lengths=("uniform", 1, 3000))
+    check_decode(w, part=part)
+
+
+def test_gqa_matrix_core_edges():
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1024, 1025]
+    w = synth.make_decode("long_gqa", device=DEV, S=len(lens), NB=4096, lengths=("fixed", lens))
+    for part in (0, 32, 128, 512):
+        check_decode(w, part=part)
+
+
+def test_gqa_matrix_core_length_one_exact():
+    w = synth.make_decode("long_gqa", device=DEV, S=5, NB=64, lengths=("fixed", [1] * 5))
+    out, _, _, _ = run_step(w)
+    expect = w.new_value.repeat_interleave(w.Hq // w.Hkv, dim=1)
+    assert torch.equal(bits(out), bits(expect))
