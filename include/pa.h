@@ -96,7 +96,7 @@ int pa_reshape_and_cache(const void* key, const void* value,
  * values from scattered blocks).
  *
  * Split context.  partition_tokens = 0 reads each sequence in one pass.
- * partition_tokens = P > 0 (a multiple of 256) cuts each context into
+ * partition_tokens = P > 0 (a multiple of bs) cuts each context into
  * P-token partitions, one workgroup each, which write their softmax max,
  * sum and unnormalised output to `workspace`; a second kernel combines
  * them.  Sequences that fit one partition are written directly.
@@ -118,7 +118,10 @@ int pa_reshape_and_cache(const void* key, const void* value,
  *   workspace        device, at least pa_decode_workspace_bytes(...) bytes,
  *                    256-byte aligned; may be NULL when that size is 0.
  * Supported: dtype any; D in {64, 128}; bs in {8, 16, 32};
- *            Hq / Hkv in {1, 2, 4, 8}. */
+ *            Hq / Hkv in {1, 2, 4, 8}.  Grouped heads with Hq / Hkv = 8,
+ *            D = 128, f16 / bf16 and partition_tokens a multiple of 32 (or
+ *            0) run both products on the matrix cores; every other shape
+ *            runs on the vector ALUs. */
 size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
                                  int32_t max_context_len, int32_t partition_tokens);
 
@@ -131,6 +134,31 @@ int pa_decode_attention(void* out, const void* query,
                         int32_t partition_tokens,
                         void* workspace, size_t workspace_bytes,
                         int32_t dtype, void* stream);
+
+/* Fused decode step: the cache write of each sequence's new token and the
+ * decode attention over its context, in one pass ("Virtual memory for
+ * attention": the token goes into the slot its block table gives it, then
+ * keys and values are gathered from the blocks).  For every sequence s with
+ * c = context_lens[s] >= 1, key[s] / value[s] ([Hkv][D]) are stored at
+ * logical position c-1, i.e. block block_tables[s][(c-1)/bs], offset
+ * (c-1)%bs (skipped if that entry is outside [0, NB)), and out[s] is the
+ * attention over c tokens including the new one.  The result, pools
+ * included, is bit-identical to pa_reshape_and_cache with those slots
+ * followed by pa_decode_attention; one launch is saved and the new rows are
+ * used from registers rather than read back.
+ *   key, value       device, [S][Hkv][D] of `dtype`.
+ *   key_cache,
+ *   value_cache      device, written at the S new slots only.
+ * Every other argument, and the supported set, as for pa_decode_attention. */
+int pa_decode_step(void* out, const void* query, const void* key, const void* value,
+                   void* key_cache, void* value_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t bs, int32_t NB, int32_t MB,
+                   int32_t max_context_len, float scale,
+                   int32_t partition_tokens,
+                   void* workspace, size_t workspace_bytes,
+                   int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Block copy for copy-on-write ("Virtual memory for attention": a completion

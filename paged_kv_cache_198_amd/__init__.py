@@ -7,8 +7,9 @@ the computation runs in the library's HIP kernels or its C++ allocator.  There
 is no fallback: if ``libpa.so`` is missing, every call raises.
 
 Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_decode_attention``,
-``pa_decode_workspace_bytes``, ``pa_copy_blocks``; ``Allocator`` wraps the
-``pa_alloc_*`` / ``pa_seq_*`` calls.
+``pa_decode_step`` (the two fused), ``pa_decode_workspace_bytes``,
+``pa_copy_blocks``; ``Allocator`` wraps the ``pa_alloc_*`` / ``pa_seq_*``
+calls.
 """
 from __future__ import annotations
 
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "pa_decode_attention": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
                                      _c_i32, _c_p, ctypes.c_size_t, _c_i32, _c_p]),
+    "pa_decode_step": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                _c_i32, _c_p, ctypes.c_size_t, _c_i32, _c_p]),
     "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
                                 _c_i32, _c_i32, _c_i64, _c_p]),
     "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
@@ -189,6 +193,44 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, key_cache: torch
         int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
         _stream(stream))
     _check(rc, "pa_decode_attention")
+
+
+def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, max_context_len: int, scale: float,
+                   partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Fused step: store key[s]/value[s] ([S, Hkv, D]) at position
+    context_lens[s]-1 of each sequence and attend over its whole context."""
+    dt = _kv_dtype(key_cache)
+    NB, Hkv, bs, D = key_cache.shape
+    S, Hq, Dq = query.shape
+    if Dq != D or query.dtype != key_cache.dtype:
+        raise ValueError("query must be [S, Hq, D] in the KV dtype")
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != key_cache.dtype:
+        raise ValueError("out must be [S, Hq, D] in the KV dtype")
+    for name, t in (("key", key), ("value", value)):
+        if tuple(t.shape) != (S, Hkv, D) or t.dtype != key_cache.dtype:
+            raise ValueError(f"{name} must be [S, {Hkv}, {D}] {key_cache.dtype}")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, MB]")
+    if tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be [S]")
+    MB = block_tables.shape[1]
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().pa_decode_step(
+        _dev(out, "out"), _dev(query, "query"), _dev(key, "key"), _dev(value, "value"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
+        _stream(stream))
+    _check(rc, "pa_decode_step")
 
 
 def make_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_tokens: int,

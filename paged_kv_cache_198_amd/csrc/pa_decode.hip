@@ -112,6 +112,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int last_lb = end > 0 ? (end - 1) / BS : 0;
   const int wv = __builtin_amdgcn_readfirstlane(w);
 
+  // Fused step: this workgroup owns position ctx-1 (the last partition).
+  // In the tile that holds the position, the lanes of its row take the new
+  // K/V rows of head g from the inputs instead of the pool and store them
+  // into the slot.
+  const bool append = a.new_key != nullptr && ctx > 0 && p == nparts - 1;
+
   for (int t0 = start + wv * TILE; t0 < end; t0 += kWaves * TILE) {
     size_t off[NL];
     bool bok[NL];
@@ -144,6 +150,25 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
         }
         kr[j] = kv;
         vr[j] = vv;
+      }
+    }
+    if (append && t0 <= ctx - 1 && ctx - 1 < t0 + TILE) {
+      const int rel = ctx - 1 - t0;
+      if (r == rel % RPW) {
+        const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * D * EB + c * 16;
+        const uint4 nk = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_key) + src);
+        const uint4 nv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_value) + src);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          if (j == rel / RPW) {
+            kr[j] = nk;
+            vr[j] = nv;
+            if (bok[j]) {
+              *reinterpret_cast<uint4*>(const_cast<char*>(kb) + off[j] + lane_off) = nk;
+              *reinterpret_cast<uint4*>(const_cast<char*>(vb) + off[j] + lane_off) = nv;
+            }
+          }
+        }
       }
     }
 
@@ -254,11 +279,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Combine the partitions of sequences longer than one partition.
+// Combine the partitions of sequences longer than one partition.  One
+// workgroup per (query head, sequence) and one thread per output element.
+// The per-partition max and sum are the same for the whole workgroup (read
+// with scalar loads); the partial outputs are summed with eight independent
+// accumulators so that eight loads are in flight per thread.
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
+  constexpr int U = 8;
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int d = threadIdx.x;
@@ -266,17 +296,38 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;
   const size_t base = (static_cast<size_t>(s) * a.Hq + h) * a.pmax;
+  const float* mp = a.ws_m + base;
+  const float* lp = a.ws_l + base;
+  const float* op = a.ws_o + base * D + d;
   float M = kNegInf;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_m[base + p]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float mp = a.ws_m[base + p];
-    const float sw = (mp == kNegInf) ? 0.f : fast_exp2(mp - M);
-    num = fmaf(a.ws_o[(base + p) * D + d], sw, num);
-    den = fmaf(a.ws_l[base + p], sw, den);
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, mp[p]);
+  float num[U], den[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) num[k] = den[k] = 0.f;
+  int p = 0;
+  for (; p + U <= nparts; p += U) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const float mk = mp[p + k];
+      const float sw = (mk == kNegInf) ? 0.f : fast_exp2(mk - M);
+      num[k] = fmaf(op[static_cast<size_t>(p + k) * D], sw, num[k]);
+      den[k] = fmaf(lp[p + k], sw, den[k]);
+    }
+  }
+  for (; p < nparts; ++p) {
+    const float mk = mp[p];
+    const float sw = (mk == kNegInf) ? 0.f : fast_exp2(mk - M);
+    num[0] = fmaf(op[static_cast<size_t>(p) * D], sw, num[0]);
+    den[0] = fmaf(lp[p], sw, den[0]);
+  }
+  float nt = 0.f, dn = 0.f;
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    nt += num[k];
+    dn += den[k];
   }
   static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * D + d] =
-      narrow<DT>(den > 0.f ? num / den : 0.f);
+      narrow<DT>(dn > 0.f ? nt / dn : 0.f);
 }
 
 template <int DT, int D, int BS, int G>
@@ -358,13 +409,15 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
   return 2 * pa::align256(n * sizeof(float)) + pa::align256(n * D * sizeof(float));
 }
 
-extern "C" int pa_decode_attention(void* out, const void* query, const void* key_cache,
-                                   const void* value_cache, const int32_t* block_tables,
-                                   const int32_t* context_lens, int32_t S, int32_t Hq,
-                                   int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
-                                   int32_t max_context_len, float scale,
-                                   int32_t partition_tokens, void* workspace,
-                                   size_t workspace_bytes, int32_t dtype, void* stream) {
+namespace pa {
+namespace {
+
+int decode_impl(void* out, const void* query, const void* new_key, const void* new_value,
+                const void* key_cache, const void* value_cache, const int32_t* block_tables,
+                const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                int32_t bs, int32_t NB, int32_t MB, int32_t max_context_len, float scale,
+                int32_t partition_tokens, void* workspace, size_t workspace_bytes, int32_t dtype,
+                void* stream) {
   if (pa::elem_bytes(dtype) == 0) return PA_ERR_INVALID;
   if (S < 0 || Hq < 1 || Hkv < 1 || D < 1 || bs < 1 || NB < 1 || MB < 1) return PA_ERR_INVALID;
   if (max_context_len < 1 || partition_tokens < 0) return PA_ERR_INVALID;
@@ -405,6 +458,8 @@ extern "C" int pa_decode_attention(void* out, const void* query, const void* key
   a.part_tokens = pmax > 1 ? partition_tokens : 0;
   a.pmax = pmax;
   a.qscale = scale * pa::kLog2e;
+  a.new_key = new_key;
+  a.new_value = new_value;
   if (pmax > 1) {
     const size_t need = pa_decode_workspace_bytes(S, Hq, D, eff_ctx, partition_tokens);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
@@ -436,4 +491,33 @@ extern "C" int pa_decode_attention(void* out, const void* query, const void* key
     case PA_F16: return pa::dispatch_reduce_d<PA_F16>(a, D, bs, st);
     default: return pa::dispatch_reduce_d<PA_BF16>(a, D, bs, st);
   }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_decode_attention(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t S, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                                   int32_t max_context_len, float scale,
+                                   int32_t partition_tokens, void* workspace,
+                                   size_t workspace_bytes, int32_t dtype, void* stream) {
+  return pa::decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                         context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
+                         partition_tokens, workspace, workspace_bytes, dtype, stream);
+}
+
+extern "C" int pa_decode_step(void* out, const void* query, const void* key, const void* value,
+                              void* key_cache, void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                              int32_t max_context_len, float scale, int32_t partition_tokens,
+                              void* workspace, size_t workspace_bytes, int32_t dtype,
+                              void* stream) {
+  if (S > 0 && (!key || !value || !pa::aligned16(key) || !pa::aligned16(value)))
+    return PA_ERR_INVALID;
+  return pa::decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
+                         context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
+                         partition_tokens, workspace, workspace_bytes, dtype, stream);
 }

@@ -188,6 +188,11 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   const int wv = __builtin_amdgcn_readfirstlane(w);
   char* vt = smem + w * (kMTile * kVRow);
 
+  // Fused step: the last partition owns position ctx-1.  In the tile that
+  // holds it, the lanes of its row take the new K/V rows of head g from the
+  // inputs instead of the pool and store them into the slot.
+  const bool append = a.new_key != nullptr && ctx > 0 && p == nparts - 1;
+
   // Issue every load of the tile at t0.  Each block's head tile is one buffer
   // resource; a row past the context, or in a block outside the pool, gets
   // an offset past the resource's end and loads zero without touching
@@ -222,6 +227,35 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
       const uint32_t voff =
           t0 + rel < end ? static_cast<uint32_t>((rel % BS) * (kMD * 2) + 16 * n) : kOutOfRange;
       tl.vr[j] = buffer_load16(vres[(4 * j) / BS], voff);
+    }
+    if (append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile) {
+      const int rel = ctx - 1 - t0;
+      if (q == rel % 4) {
+        const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * kMD * 2 + 16 * n;
+        const uint4 nk = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_key) + src);
+        const uint4 nv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_value) + src);
+        const int bi = (rel - rel % 4) / BS;          // block of the row group (uniform)
+        int b = blk[0];
+        bool bvalid = tl.bok[0];
+#pragma unroll
+        for (int k = 1; k < NBK; ++k) {
+          b = (k == bi) ? blk[k] : b;
+          bvalid = (k == bi) ? tl.bok[k] : bvalid;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j == rel / 4) {
+            tl.kr[j] = nk;
+            tl.vr[j] = nv;
+          }
+        }
+        if (bvalid) {
+          const size_t dst = static_cast<size_t>(b) * bstride +
+                             static_cast<size_t>(rel % BS) * (kMD * 2) + 16 * n;
+          *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) = nk;
+          *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
+        }
+      }
     }
   };
 

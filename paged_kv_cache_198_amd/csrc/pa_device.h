@@ -116,6 +116,11 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   float* ws_o;
+  // Fused step (pa_decode_step): the token at position ctx-1 of each
+  // sequence, [S][Hkv][D]; null for plain attention.  The workgroup that
+  // owns that position writes it into its slot and uses it from registers.
+  const void* new_key;
+  const void* new_value;
   int32_t S, Hq, Hkv, NB, MB, max_ctx;
   int32_t part_tokens;  // 0: one pass over the whole context
   int32_t pmax;         // partitions per sequence in the grid / workspace

@@ -499,3 +499,50 @@ def test_gqa_matrix_core_length_one_exact():
     out, _, _, _ = run_step(w)
     expect = w.new_value.repeat_interleave(w.Hq // w.Hkv, dim=1)
     assert torch.equal(bits(out), bits(expect))
+
+
+# ---------------------------------------------------------------------------
+# fused step: pa_decode_step must equal pa_reshape_and_cache + pa_decode_attention
+# bit for bit (outputs and whole pools), on both kernels, with and without
+# partitions, and the oracle bound must hold for it directly
+# ---------------------------------------------------------------------------
+def run_fused(w, part):
+    step, tables, lens = lib_slots(w)
+    kc, vc = w.key_cache.clone(), w.value_cache.clone()
+    out = torch.full((w.S, w.Hq, w.D), float("nan"), dtype=w.q.dtype, device=DEV)
+    ws = pa.make_workspace(w.S, w.Hq, w.D, w.max_context_len, part)
+    pa.pa_decode_step(out, w.q, w.new_key, w.new_value, kc, vc, torch.from_numpy(tables).to(DEV),
+                      torch.from_numpy(lens).to(DEV), w.max_context_len, w.scale, part, ws)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+FUSED_CASES = [
+    ("tiny", {}, 0), ("tiny", dict(S=7, NB=96), 32),
+    ("llama13b", dict(bs=8, S=6, pool_tokens=16384), 0),
+    ("llama13b", dict(bs=16, S=6, pool_tokens=16384), 256),
+    ("llama13b", dict(bs=32, S=6, pool_tokens=16384, lengths=("fixed", [1, 32, 33, 64, 700, 2048])), 0),
+    ("llama7b", dict(S=5, NB=512, Hq=4, Hkv=4, D=128, dtype="f32", lengths=("uniform", 1, 900)), 0),
+    ("long_gqa", dict(S=3, NB=1024, lengths=("uniform", 700, 4000)), 512),
+    ("long_gqa", dict(S=4, NB=1024, lengths=("fixed", [1, 31, 32, 1025])), 0),
+    ("long_gqa", dict(S=3, NB=2048, bs=8, dtype="f16", lengths=("uniform", 1, 3000)), 64),
+]
+
+
+@pytest.mark.parametrize("name,over,part", FUSED_CASES)
+def test_fused_step_equals_two_calls(name, over, part):
+    w = synth.make_decode(name, device=DEV, **over)
+    note(f"case fused {name} {over} part={part}")
+    out1, kc1, vc1, _ = run_step(w, part)
+    out2, kc2, vc2 = run_fused(w, part)
+    assert torch.equal(bits(out1), bits(out2))
+    assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+
+
+def test_fused_step_against_oracle():
+    w = synth.make_decode("llama13b", device=DEV, S=8, pool_tokens=16384)
+    out, _, _ = run_fused(w, 0)
+    ref, _ = oracle_step(w)
+    err = float(np.max(np.abs(widened(out, w.dtype) - ref)))
+    note(f"  fused max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
