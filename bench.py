@@ -53,12 +53,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b",
-                    choices=["llama13b", "llama7b", "long_gqa", "tiny"],
+                    choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix"],
                     help="decode workload to time (default: the 13B-shaped batch)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition tokens (0 = single pass, -1 = library default for the shape)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prompt-len", type=int, default=504,
+                    help="shared_prefix: prompt tokens (504 leaves the last shared block "
+                         "half full, so forks copy it; 512 fills it)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the plain HBM probe")
@@ -242,6 +245,93 @@ def calibrate_copy(torch):
     torch.cuda.synchronize()
 
 
+def run_shared_prefix(args, pa, synth, torch):
+    """Parallel sampling: 16 prompts x 4 samples sharing the prompt's blocks.
+    Setup (prefill, fork, per-sample tails with copy-on-write) runs through the
+    library's allocator and kernels; then every sample reserves its next slot
+    and K fused decode steps are timed.  Reports logical bytes (each sample
+    reads its prompt) and unique bytes (shared blocks counted once)."""
+    from paged_kv_cache_198_amd import engine
+    sc = synth.make_shared_prefix(seed=args.seed, device="cuda", prompt_len=args.prompt_len)
+    kv = engine.build_shared_prefix(sc)
+    fork_copies = kv.copies
+    seqs = list(range(sc.S))
+    _, pairs = kv.reserve(seqs)
+    tables, lens, mx = kv.batch(seqs)
+    out = torch.empty(sc.S, sc.Hq, sc.D, dtype=sc.q.dtype, device="cuda")
+
+    def step():
+        pa.pa_decode_step(out, sc.q, sc.step_k, sc.step_v, kv.key_cache, kv.value_cache,
+                          tables, lens, mx, sc.scale, 0, None)
+
+    for _ in range(args.warmup):
+        step()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    eb = synth.ELEM_BYTES[sc.dtype]
+    lens_h = lens.cpu().numpy().astype(np.int64)
+    logical = int(lens_h.sum()) * 2 * sc.Hkv * sc.D * eb
+    unique_blocks = kv.used_blocks()
+    block_bytes = sc.bs * sc.Hkv * sc.D * eb
+    unique = unique_blocks * 2 * block_bytes
+    private_blocks = kv.logical_blocks(seqs)
+
+    # copy-on-write block copies across the layers of a 40-layer model: the
+    # fork-time divergence of this batch (one pair per sample that writes
+    # into its prompt's half-filled last block) copied in every layer
+    L, nb_l = 40, 512
+    pools_k = [torch.empty(nb_l, sc.Hkv, sc.bs, sc.D, dtype=sc.q.dtype, device="cuda")
+               for _ in range(L)]
+    pools_v = [torch.empty_like(pools_k[0]) for _ in range(L)]
+    n_pairs = max(fork_copies, 1)
+    perm = np.random.default_rng(args.seed).permutation(nb_l)
+    cow = np.stack([perm[:n_pairs], perm[n_pairs:2 * n_pairs]], axis=1)
+    for _ in range(3):
+        pa.pa_copy_blocks(pools_k, pools_v, cow)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(20):
+        pa.pa_copy_blocks(pools_k, pools_v, cow)
+    stop.record()
+    torch.cuda.synchronize()
+    cow_ms = start.elapsed_time(stop) / 20
+    cow_bytes = 2 * n_pairs * L * 2 * block_bytes          # read + write, K and V
+    return {
+        "metric": "decode-attention KV GB/s (frac of MI355X HBM peak) + us/step, shared-prefix batch",
+        "value": logical / (step_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "us_per_step": step_ms * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": sc.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, uniform tails)",
+        "config": {"workload": f"shared-prefix parallel sampling: {sc.prompts} prompts x "
+                               f"{sc.samples} samples, Hq=Hkv={sc.Hkv}, D={sc.D}, {sc.dtype}, "
+                               f"block_size {sc.bs}, prompt {sc.prompt_len} tokens in shared "
+                               f"blocks, tails uniform in [0, 256], {sc.NB}-block pool",
+                   "S": sc.S, "prompt_len": sc.prompt_len, "seed": args.seed,
+                   "logical_kv_bytes": logical, "unique_kv_bytes": unique},
+        "unique_GBs": unique / (step_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": logical / (step_ms * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": logical / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "frac_unique": unique / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "pa::decode_kernel (pa_decode_step)",
+                     "note": "logical bytes count each sample's reads of its shared prompt; "
+                             "shared blocks may be served from L2 / MALL"},
+        "sharing": {"blocks_used": unique_blocks, "blocks_if_private": private_blocks,
+                    "memory_saving": 1.0 - unique_blocks / private_blocks,
+                    "cow_copies_at_fork": fork_copies, "cow_pairs_this_step": len(pairs)},
+        "cow_copy": {"pairs": n_pairs, "layers": L, "us": cow_ms * 1e3,
+                     "GBs": cow_bytes / (cow_ms * 1e-3) / 1e9},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +346,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     pa.lib()
+    if args.workload == "shared_prefix":
+        print("[bench] building shared-prefix state", file=sys.stderr, flush=True)
+        print(json.dumps(run_shared_prefix(args, pa, synth, torch)), flush=True)
+        return
     print(f"[bench] building workload {args.workload} bs={args.bs}", file=sys.stderr, flush=True)
     st = Step(pa, synth, torch, args.bs, args.seed, args.partition, args.workload)
     w = st.w
@@ -266,13 +360,17 @@ def main():
 
     sweep = {}
     if not args.no_sweep and args.workload == "llama13b":
-        for bs in (8, 16, 32):
+        for bs in (8, 16, 32, 64, 128):
             if bs == args.bs:
                 continue
             print(f"[bench] sweep bs={bs}", file=sys.stderr, flush=True)
             other = Step(pa, synth, torch, bs, args.seed, args.partition)
             s_ms, _ = other.run(max(20, args.steps // 4), args.warmup, fused=True)
+            lens_h = other.lens.cpu().numpy().astype(np.int64)
+            blocks = (lens_h + bs - 1) // bs
             sweep[f"bs{bs}"] = {"us_per_step": s_ms * 1e3,
+                                "tail_waste": float((blocks * bs - lens_h).sum()
+                                                    / (blocks * bs).sum()),
                                 "GBs": other.kv_bytes / (s_ms * 1e-3) / 1e9,
                                 "frac_hbm_peak": other.kv_bytes / (s_ms * 1e-3) / 1e9
                                 / HBM_PEAK_GBS}

@@ -117,7 +117,7 @@ int pa_reshape_and_cache(const void* key, const void* value,
  *   scale            logit scale (e.g. 1/sqrt(D)).
  *   workspace        device, at least pa_decode_workspace_bytes(...) bytes,
  *                    256-byte aligned; may be NULL when that size is 0.
- * Supported: dtype any; D in {64, 128}; bs in {8, 16, 32};
+ * Supported: dtype any; D in {64, 128}; bs in {8, 16, 32, 64, 128};
  *            Hq / Hkv in {1, 2, 4, 8}.  Grouped heads with Hq / Hkv = 8,
  *            D = 128, f16 / bf16 and partition_tokens a multiple of 32 (or
  *            0) run both products on the matrix cores; every other shape

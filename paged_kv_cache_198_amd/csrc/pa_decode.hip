@@ -353,6 +353,8 @@ int dispatch_reduce(const DecodeArgs& a, int bs, hipStream_t st) {
     case 8: return launch_reduce<DT, D, 8>(a, st);
     case 16: return launch_reduce<DT, D, 16>(a, st);
     case 32: return launch_reduce<DT, D, 32>(a, st);
+    case 64: return launch_reduce<DT, D, 64>(a, st);
+    case 128: return launch_reduce<DT, D, 128>(a, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -379,6 +381,8 @@ int dispatch_bs(const DecodeArgs& a, int bs, int G, hipStream_t st) {
     case 8: return dispatch_g<DT, D, 8>(a, G, st);
     case 16: return dispatch_g<DT, D, 16>(a, G, st);
     case 32: return dispatch_g<DT, D, 32>(a, G, st);
+    case 64: return dispatch_g<DT, D, 64>(a, G, st);
+    case 128: return dispatch_g<DT, D, 128>(a, G, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -435,7 +439,7 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
     return PA_ERR_INVALID;
   const int G = Hq / Hkv;
   if (D != 64 && D != 128) return PA_ERR_UNSUPPORTED;
-  if (bs != 8 && bs != 16 && bs != 32) return PA_ERR_UNSUPPORTED;
+  if (bs != 8 && bs != 16 && bs != 32 && bs != 64 && bs != 128) return PA_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
   const int32_t eff_ctx = static_cast<int32_t>(
       std::min<int64_t>(max_context_len, static_cast<int64_t>(MB) * bs));

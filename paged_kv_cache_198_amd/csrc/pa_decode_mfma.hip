@@ -130,8 +130,10 @@ template <int DT, int BS>
 __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
-  constexpr int NBK = kMTile / BS;         // blocks per tile (bs divides 32)
-  static_assert(kMTile % BS == 0 && BS >= 4, "block size");
+  // A tile spans 32/bs blocks when bs divides 32, else it sits inside one
+  // block at offset t0 % bs (a multiple of 32).
+  constexpr int NBK = BS >= kMTile ? 1 : kMTile / BS;
+  static_assert((kMTile % BS == 0 || BS % kMTile == 0) && BS >= 4, "block size");
   using Tile = TileRegs<NBK>;
 
   // Per-wavefront K/V tiles during the loop; the same bytes hold the
@@ -198,6 +200,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   // an offset past the resource's end and loads zero without touching
   // memory, so no load sits behind a branch.
   auto issue = [&](int t0, Tile& tl) {
+    const int boff = BS > kMTile ? t0 % BS : 0;   // tile's row offset in its first block
     int blk[NBK];
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
@@ -218,15 +221,17 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
     for (int j = 0; j < 8; ++j) {
       const int rel = 4 * j + q;
       const uint32_t voff =
-          t0 + rel < end ? static_cast<uint32_t>((rel % BS) * (kMD * 2) + 16 * n) : kOutOfRange;
-      tl.kr[j] = buffer_load16(kres[(4 * j) / BS], voff);
+          t0 + rel < end ? static_cast<uint32_t>(((boff + rel) % BS) * (kMD * 2) + 16 * n)
+                         : kOutOfRange;
+      tl.kr[j] = buffer_load16(kres[(boff + 4 * j) / BS], voff);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int rel = 4 * j + q;
       const uint32_t voff =
-          t0 + rel < end ? static_cast<uint32_t>((rel % BS) * (kMD * 2) + 16 * n) : kOutOfRange;
-      tl.vr[j] = buffer_load16(vres[(4 * j) / BS], voff);
+          t0 + rel < end ? static_cast<uint32_t>(((boff + rel) % BS) * (kMD * 2) + 16 * n)
+                         : kOutOfRange;
+      tl.vr[j] = buffer_load16(vres[(boff + 4 * j) / BS], voff);
     }
     if (append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile) {
       const int rel = ctx - 1 - t0;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
         const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * kMD * 2 + 16 * n;
         const uint4 nk = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_key) + src);
         const uint4 nv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_value) + src);
-        const int bi = (rel - rel % 4) / BS;          // block of the row group (uniform)
+        const int bi = (boff + rel - rel % 4) / BS;   // block of the row group (uniform)
         int b = blk[0];
         bool bvalid = tl.bok[0];
 #pragma unroll
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
         }
         if (bvalid) {
           const size_t dst = static_cast<size_t>(b) * bstride +
-                             static_cast<size_t>(rel % BS) * (kMD * 2) + 16 * n;
+                             static_cast<size_t>((boff + rel) % BS) * (kMD * 2) + 16 * n;
           *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) = nk;
           *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
         }
@@ -286,7 +291,8 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rel = 16 * u + 4 * q + i;
-        const bool ok = t0 + rel < end && pick_ok(tl.bok, rel / BS);
+        const bool ok = t0 + rel < end &&
+                        pick_ok(tl.bok, (BS > kMTile ? t0 % BS + rel : rel) / BS);
         const float x = ok ? sc[u][i] * a.qscale : kNegInf;
         sv[4 * u + i] = x;
         mt = fmaxf(mt, x);
@@ -396,6 +402,8 @@ int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
     case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8>), grid, dim3(kMWaves * 64), 0, st, a); break;
     case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16>), grid, dim3(kMWaves * 64), 0, st, a); break;
     case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 64>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 128>), grid, dim3(kMWaves * 64), 0, st, a); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return launch_status();

@@ -65,6 +65,7 @@ def decode_call(**over):
     (dict(Hq=24, Hkv=8), pa.PA_ERR_UNSUPPORTED),
     (dict(D=96), pa.PA_ERR_UNSUPPORTED),
     (dict(bs=4), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=48), pa.PA_ERR_UNSUPPORTED),
     (dict(max_ctx=0), pa.PA_ERR_INVALID),
     (dict(part=-16), pa.PA_ERR_INVALID),
     (dict(part=24), pa.PA_ERR_INVALID),
