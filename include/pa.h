@@ -161,6 +161,90 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
                    int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Shared-prefix (cascade) decode.  "Virtual memory for attention" (parallel
+ * sampling, beam search): forked sequences keep pointing at the same
+ * physical blocks for their common prompt, and a plain decode reads those
+ * blocks once per sequence.  The cascade reads them once per group of
+ * sequences: softmax over a context split into disjoint pieces equals the
+ * weighted merge of each piece's (max, sum, unnormalised output), so the
+ * shared prefix and each sequence's own suffix are attended separately and
+ * merged by the partition reduce.
+ *
+ * pa_cascade_plan (host only, no device call) reads the batch's block tables
+ * and context lengths and builds the plan:
+ *   * sequences whose tables start with the same physical block form a
+ *     group, taken in chunks of 16 / (Hq / Hkv) members (the query heads of
+ *     one chunk fill the 16 columns of one matrix-core tile);
+ *   * a chunk's shared prefix T_sh is the run of leading table entries that
+ *     all its members hold, counting only blocks that lie wholly before
+ *     each member's last position, rounded down to a multiple of
+ *     max(bs, 32) tokens; chunks with T_sh = 0 and sequences in no chunk
+ *     are planned as in a plain decode;
+ *   * the prefix is cut into pieces of prefix_tokens tokens (a multiple of
+ *     max(bs, 32); 0 = one piece), one work item each;
+ *   * each sequence's suffix [T_sh, ctx) is cut into partitions of
+ *     partition_tokens tokens (a multiple of bs; 0 = one partition).
+ * Inputs:
+ *   block_tables     host int32 [S][MB], as for pa_decode_attention.
+ *   context_lens     host int32 [S] (clamped to [0, MB*bs]).
+ * Outputs:
+ *   plan             host int32, plan_ints entries: seq_start[S] (T_sh or
+ *                    0), slot_base[S] (prefix pieces before the suffix
+ *                    partitions), then n_items work items of
+ *                    PA_CASCADE_ITEM_INTS ints: table sequence, token start,
+ *                    token end, partial slot, member count, 16 member
+ *                    sequences (unused ones -1).
+ *   info             host int32 [PA_CASCADE_INFO_INTS]: n_items, slots_max
+ *                    (partial slots per sequence and head), suffix_parts
+ *                    (most suffix partitions of any sequence), plan ints
+ *                    needed, prefix rows read by the group pass, rows the
+ *                    members would have read on top of that in a plain
+ *                    decode.
+ * Returns PA_ERR_WORKSPACE (with info filled in) when plan is NULL or
+ * shorter than info[3]; call again with a plan that large. */
+#define PA_CASCADE_ITEM_INTS 21
+#define PA_CASCADE_INFO_INTS 6
+int pa_cascade_plan(const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t S, int32_t MB, int32_t bs, int32_t Hq, int32_t Hkv,
+                    int32_t partition_tokens, int32_t prefix_tokens,
+                    int32_t* plan, size_t plan_ints, int32_t* info);
+
+/* Workspace for pa_decode_cascade: partial (max, sum, output) slots for
+ * S * Hq * slots_max entries; 0 when slots_max <= 1. */
+size_t pa_cascade_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t slots_max);
+
+/* Decode attention (and, when key / value are given, the fused store of the
+ * new token as in pa_decode_step) following a plan from pa_cascade_plan.
+ * Up to three launches on `stream`: the prefix pass (matrix cores, one
+ * workgroup per work item and KV head), the suffix pass (the same kernels as
+ * pa_decode_attention, starting at seq_start), and the partition reduce.
+ *   plan             device int32 copy of the plan's first
+ *                    2*S + n_items*PA_CASCADE_ITEM_INTS ints.
+ *   n_items,
+ *   slots_max,
+ *   suffix_parts     info[0..2] of the plan.
+ *   key, value       device [S][Hkv][D] new rows, or both NULL for
+ *                    attention only.
+ *   workspace        device, pa_cascade_workspace_bytes(...) bytes,
+ *                    256-byte aligned.
+ * The plan must have been built from the same block tables and lengths:
+ * entries are bounds-checked on the device (a bad plan gives wrong numbers,
+ * never an access outside the pools or the workspace) but not validated.
+ * Supported: f16 / bf16, D = 128, Hq / Hkv in {1, 2, 4, 8}, bs as for
+ * pa_decode_attention; every other argument as there. */
+int pa_decode_cascade(void* out, const void* query, const void* key, const void* value,
+                      void* key_cache, void* value_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* plan, int32_t n_items, int32_t slots_max,
+                      int32_t suffix_parts,
+                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                      int32_t bs, int32_t NB, int32_t MB,
+                      int32_t max_context_len, float scale,
+                      int32_t partition_tokens,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Block copy for copy-on-write ("Virtual memory for attention": a completion
  * that diverges from a shared block gets its own copy).  For every pair
  * (src, dst) and every layer l, key block dst becomes a copy of key block

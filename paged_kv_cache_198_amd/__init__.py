@@ -8,7 +8,8 @@ is no fallback: if ``libpa.so`` is missing, every call raises.
 
 Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_decode_attention``,
 ``pa_decode_step`` (the two fused), ``pa_decode_workspace_bytes``,
-``pa_copy_blocks``; ``Allocator`` wraps the ``pa_alloc_*`` / ``pa_seq_*``
+``pa_copy_blocks``, ``pa_cascade_plan`` / ``pa_decode_cascade`` (shared-prefix
+decode); ``Allocator`` wraps the ``pa_alloc_*`` / ``pa_seq_*``
 calls.
 """
 from __future__ import annotations
@@ -48,6 +49,13 @@ _SIGNATURES = {
     "pa_decode_step": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
                                 _c_i32, _c_p, ctypes.c_size_t, _c_i32, _c_p]),
+    "pa_cascade_plan": (_c_int, [_p_i32, _p_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                 _c_i32, _p_i32, ctypes.c_size_t, _p_i32]),
+    "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_cascade": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                   _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t,
+                                   _c_i32, _c_p]),
     "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
                                 _c_i32, _c_i32, _c_i64, _c_p]),
     "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
@@ -240,6 +248,122 @@ def make_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_toke
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix (cascade) decode
+# ---------------------------------------------------------------------------
+CASCADE_ITEM_INTS = 21
+CASCADE_INFO_INTS = 6
+
+
+class CascadePlan:
+    """A plan from ``pa_cascade_plan``: ``plan`` (host int32: seq_start[S],
+    slot_base[S], then n_items work items of 21 ints) and its sizes."""
+
+    def __init__(self, S: int, plan: np.ndarray, info: np.ndarray):
+        self.S = S
+        self.plan = plan
+        self.n_items, self.slots_max, self.suffix_parts = (int(x) for x in info[:3])
+        self.prefix_rows, self.saved_rows = int(info[4]), int(info[5])
+        self._dev = None
+
+    @property
+    def seq_start(self) -> np.ndarray:
+        return self.plan[:self.S]
+
+    @property
+    def slot_base(self) -> np.ndarray:
+        return self.plan[self.S:2 * self.S]
+
+    @property
+    def items(self) -> np.ndarray:
+        return self.plan[2 * self.S:].reshape(-1, CASCADE_ITEM_INTS)
+
+    def device(self, device="cuda") -> torch.Tensor:
+        """The plan as a device tensor (copied once)."""
+        if self._dev is None or str(self._dev.device) != str(torch.device(device)):
+            src = self.plan if self.plan.size else np.zeros(1, dtype=np.int32)
+            self._dev = torch.from_numpy(src).to(device)
+        return self._dev
+
+
+def pa_cascade_plan(block_tables: np.ndarray, context_lens: np.ndarray, bs: int, Hq: int,
+                    Hkv: int, partition_tokens: int = 0, prefix_tokens: int = 0) -> CascadePlan:
+    """Plan the shared-prefix decode of a batch from its host block tables
+    ([S, MB] int32) and context lengths ([S] int32)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or cl.shape != (bt.shape[0],):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    S, MB = bt.shape
+    info = np.zeros(CASCADE_INFO_INTS, dtype=np.int32)
+    pi32 = lambda a: a.ctypes.data_as(_p_i32)
+    args = (pi32(bt), pi32(cl), S, MB, bs, Hq, Hkv, partition_tokens, prefix_tokens)
+    rc = lib().pa_cascade_plan(*args, None, 0, pi32(info))
+    if rc != PA_ERR_WORKSPACE:
+        _check(rc, "pa_cascade_plan")
+    plan = np.zeros(int(info[3]), dtype=np.int32)
+    _check(lib().pa_cascade_plan(*args, pi32(plan), plan.size, pi32(info)), "pa_cascade_plan")
+    return CascadePlan(S, plan, info)
+
+
+def pa_cascade_workspace_bytes(S: int, Hq: int, D: int, slots_max: int) -> int:
+    return int(lib().pa_cascade_workspace_bytes(S, Hq, D, slots_max))
+
+
+def make_cascade_workspace(S: int, Hq: int, D: int, plan: CascadePlan,
+                           device="cuda") -> Optional[torch.Tensor]:
+    n = pa_cascade_workspace_bytes(S, Hq, D, plan.slots_max)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_decode_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, plan: CascadePlan, max_context_len: int,
+                      scale: float, partition_tokens: int = 0,
+                      workspace: Optional[torch.Tensor] = None,
+                      key: Optional[torch.Tensor] = None, value: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Decode attention along a shared-prefix plan; with ``key``/``value``
+    ([S, Hkv, D]) the new token is stored as in ``pa_decode_step``."""
+    dt = _kv_dtype(key_cache)
+    NB, Hkv, bs, D = key_cache.shape
+    S, Hq, Dq = query.shape
+    if Dq != D or query.dtype != key_cache.dtype:
+        raise ValueError("query must be [S, Hq, D] in the KV dtype")
+    if tuple(out.shape) != (S, Hq, D) or out.dtype != key_cache.dtype:
+        raise ValueError("out must be [S, Hq, D] in the KV dtype")
+    if (key is None) != (value is None):
+        raise ValueError("give both key and value, or neither")
+    kp = vp = None
+    if key is not None:
+        for name, t in (("key", key), ("value", value)):
+            if tuple(t.shape) != (S, Hkv, D) or t.dtype != key_cache.dtype:
+                raise ValueError(f"{name} must be [S, {Hkv}, {D}] {key_cache.dtype}")
+        kp, vp = _dev(key, "key"), _dev(value, "value")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, MB]")
+    if tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be [S]")
+    if plan.S != S:
+        raise ValueError("plan was built for another batch")
+    MB = block_tables.shape[1]
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    pd = plan.device(query.device)
+    rc = lib().pa_decode_cascade(
+        _dev(out, "out"), _dev(query, "query"), kp, vp, _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), _dev(pd, "plan", torch.int32),
+        plan.n_items, plan.slots_max, plan.suffix_parts, S, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
+        _stream(stream))
+    _check(rc, "pa_decode_cascade")
 
 
 def pa_copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_abi.cpp", "pa_alloc.cpp", "pa_cache_ops.hip", "pa_decode.hip", "pa_decode_mfma.hip"]
+SOURCES = ["pa_abi.cpp", "pa_alloc.cpp", "pa_cascade.cpp", "pa_cache_ops.hip", "pa_decode.hip",
+           "pa_decode_mfma.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-result"]

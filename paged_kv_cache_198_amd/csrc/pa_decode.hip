@@ -73,11 +73,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int c = lane - r * RL;
 
   const int ctx = clamp_ctx(a, s, BS);
-  const int PT = a.part_tokens > 0 ? a.part_tokens : max(ctx, 1);
-  const int nparts = max(1, (ctx + PT - 1) / PT);
+  const PartRange pr = part_range(a, s, p, ctx, BS > 32 ? BS : 32);
+  const int nparts = pr.nparts;
   if (p >= nparts) return;
-  const int start = p * PT;
-  const int end = min(ctx, start + PT);
+  const int start = pr.start;
+  const int end = pr.end;
 
   float qf[G][VEC];
   {
@@ -265,11 +265,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       den = fmaf(red_l[v][gi], sw, den);
     }
     const int h = g * G + gi;
-    if (nparts == 1) {
+    if (pr.total == 1) {
       static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * D + d] =
           narrow<DT>(den > 0.f ? num / den : 0.f);
-    } else {
-      const size_t idx = (static_cast<size_t>(s) * a.Hq + h) * a.pmax + p;
+    } else if (pr.slot < a.pmax) {
+      const size_t idx = (static_cast<size_t>(s) * a.Hq + h) * a.pmax + pr.slot;
       a.ws_o[idx * D + d] = num;
       if (d == 0) {
         a.ws_m[idx] = M;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
   const int s = blockIdx.y;
   const int d = threadIdx.x;
   const int ctx = clamp_ctx(a, s, BS);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  const int nparts = part_range(a, s, 0, ctx, BS > 32 ? BS : 32).total;
   if (nparts <= 1) return;
   const size_t base = (static_cast<size_t>(s) * a.Hq + h) * a.pmax;
   const float* mp = a.ws_m + base;
@@ -334,7 +334,7 @@ template <int DT, int D, int BS, int G>
 int launch_decode(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_kernel<DT, D, BS, G>),
                      dim3(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
-                          static_cast<uint32_t>(a.pmax)),
+                          static_cast<uint32_t>(a.grid_parts)),
                      dim3(kWaves * 64), 0, st, a);
   return launch_status();
 }
@@ -413,15 +413,29 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
   return 2 * pa::align256(n * sizeof(float)) + pa::align256(n * D * sizeof(float));
 }
 
+extern "C" size_t pa_cascade_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
+                                             int32_t slots_max) {
+  if (S <= 0 || Hq <= 0 || D <= 0 || slots_max <= 1) return 0;
+  const size_t n = static_cast<size_t>(S) * Hq * slots_max;
+  return 2 * pa::align256(n * sizeof(float)) + pa::align256(n * D * sizeof(float));
+}
+
 namespace pa {
 namespace {
+
+// A cascade plan on the device (seq_start[S], slot_base[S], items) and its
+// host-side sizes.
+struct Cascade {
+  const int32_t* plan;
+  int32_t n_items, slots_max, suffix_parts;
+};
 
 int decode_impl(void* out, const void* query, const void* new_key, const void* new_value,
                 const void* key_cache, const void* value_cache, const int32_t* block_tables,
                 const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                 int32_t bs, int32_t NB, int32_t MB, int32_t max_context_len, float scale,
                 int32_t partition_tokens, void* workspace, size_t workspace_bytes, int32_t dtype,
-                void* stream) {
+                void* stream, const Cascade* cas = nullptr) {
   if (pa::elem_bytes(dtype) == 0) return PA_ERR_INVALID;
   if (S < 0 || Hq < 1 || Hkv < 1 || D < 1 || bs < 1 || NB < 1 || MB < 1) return PA_ERR_INVALID;
   if (max_context_len < 1 || partition_tokens < 0) return PA_ERR_INVALID;
@@ -443,7 +457,19 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
   if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
   const int32_t eff_ctx = static_cast<int32_t>(
       std::min<int64_t>(max_context_len, static_cast<int64_t>(MB) * bs));
-  const int32_t pmax = pa::num_partitions(eff_ctx, partition_tokens);
+  int32_t pmax = pa::num_partitions(eff_ctx, partition_tokens);
+  int32_t grid_parts = pmax;
+  if (cas) {
+    // the prefix pass runs on the matrix cores only
+    if ((dtype != PA_BF16 && dtype != PA_F16) || D != 128) return PA_ERR_UNSUPPORTED;
+    if (!cas->plan || (reinterpret_cast<uintptr_t>(cas->plan) & 3u)) return PA_ERR_INVALID;
+    if (cas->n_items < 0 || cas->slots_max < 1 || cas->suffix_parts < 1 ||
+        cas->suffix_parts > cas->slots_max || (cas->n_items > 0 && cas->slots_max < 2))
+      return PA_ERR_INVALID;
+    if (cas->n_items > 65535) return PA_ERR_UNSUPPORTED;
+    pmax = cas->slots_max;
+    grid_parts = cas->suffix_parts;
+  }
   if (S > 65535 || pmax > 65535) return PA_ERR_UNSUPPORTED;
 
   pa::DecodeArgs a{};
@@ -459,13 +485,21 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
   a.NB = NB;
   a.MB = MB;
   a.max_ctx = eff_ctx;
-  a.part_tokens = pmax > 1 ? partition_tokens : 0;
+  a.part_tokens = (pmax > 1 || cas) ? partition_tokens : 0;
   a.pmax = pmax;
+  a.grid_parts = grid_parts;
   a.qscale = scale * pa::kLog2e;
   a.new_key = new_key;
   a.new_value = new_value;
+  if (cas) {
+    a.seq_start = cas->plan;
+    a.slot_base = cas->plan + S;
+    a.items = cas->plan + 2 * static_cast<size_t>(S);
+    a.n_items = cas->n_items;
+  }
   if (pmax > 1) {
-    const size_t need = pa_decode_workspace_bytes(S, Hq, D, eff_ctx, partition_tokens);
+    const size_t need = cas ? pa_cascade_workspace_bytes(S, Hq, D, pmax)
+                            : pa_decode_workspace_bytes(S, Hq, D, eff_ctx, partition_tokens);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return PA_ERR_WORKSPACE;
     const size_t n = static_cast<size_t>(S) * Hq * pmax;
@@ -479,7 +513,9 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
   // other shape runs the vector-ALU kernel.
   const bool mfma = (dtype == PA_BF16 || dtype == PA_F16) && D == 128 && G == 8 &&
                     a.part_tokens % 32 == 0;
-  int rc;
+  int rc = PA_OK;
+  if (cas) rc = pa::launch_shared_prefix_mfma(a, dtype, bs, st);
+  if (rc != PA_OK) return rc;
   if (mfma) {
     rc = pa::launch_decode_gqa_mfma(a, dtype, bs, st);
   } else {
@@ -524,4 +560,21 @@ extern "C" int pa_decode_step(void* out, const void* query, const void* key, con
   return pa::decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
                          context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
                          partition_tokens, workspace, workspace_bytes, dtype, stream);
+}
+
+extern "C" int pa_decode_cascade(void* out, const void* query, const void* key,
+                                 const void* value, void* key_cache, void* value_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* plan, int32_t n_items, int32_t slots_max,
+                                 int32_t suffix_parts, int32_t S, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                                 int32_t max_context_len, float scale, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, int32_t dtype,
+                                 void* stream) {
+  if ((key == nullptr) != (value == nullptr)) return PA_ERR_INVALID;
+  if (key && (!pa::aligned16(key) || !pa::aligned16(value))) return PA_ERR_INVALID;
+  const pa::Cascade cas{plan, n_items, slots_max, suffix_parts};
+  return pa::decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
+                         context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
+                         partition_tokens, workspace, workspace_bytes, dtype, stream, &cas);
 }

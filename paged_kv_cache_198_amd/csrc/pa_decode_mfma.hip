@@ -126,10 +126,17 @@ struct TileRegs {
   bool bok[NBK];
 };
 
-template <int DT, int BS>
+// GROUP = false: grouped-query decode, the 8 query heads of KV head g of
+// sequence s are the tile's columns; grid (Hkv, S, partitions).
+// GROUP = true: shared-prefix pass, one work item per grid row; the columns
+// are (member sequence, query head) pairs of sequences whose block tables
+// share the item's token range, which is read once for all of them; every
+// column writes a partial to its member's workspace slot.
+template <int DT, int BS, bool GROUP>
 __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
+  constexpr int NC = GROUP ? 16 : kMG;     // columns that produce output
   // A tile spans 32/bs blocks when bs divides 32, else it sits inside one
   // block at offset t0 % bs (a multiple of 32).
   constexpr int NBK = BS >= kMTile ? 1 : kMTile / BS;
@@ -139,9 +146,9 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   // Per-wavefront K/V tiles during the loop; the same bytes hold the
   // cross-wavefront merge afterwards.
   struct Merge {
-    float o[kMWaves][kMG][kMD];
-    float m[kMWaves][kMG];
-    float l[kMWaves][kMG];
+    float o[kMWaves][NC][kMD];
+    float m[kMWaves][NC];
+    float l[kMWaves][NC];
   };
   constexpr int kTileBytes = kMWaves * kMTile * kVRow;
   constexpr int kSmem = kTileBytes > static_cast<int>(sizeof(Merge)) ? kTileBytes : sizeof(Merge);
@@ -149,29 +156,62 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   Merge& red = *reinterpret_cast<Merge*>(smem);
 
   const int g = blockIdx.x;
-  const int s = blockIdx.y;
   const int p = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int n = lane & 15;                 // head (scores, output) / token row (K) / d col
+  const int n = lane & 15;                 // column (scores, output) / token row (K) / d col
   const int q = lane >> 4;                 // lane group
 
-  const int ctx = clamp_ctx(a, s, BS);
-  const int PT = a.part_tokens > 0 ? a.part_tokens : max(ctx, 1);
-  const int nparts = max(1, (ctx + PT - 1) / PT);
-  if (p >= nparts) return;
-  const int start = p * PT;
-  const int end = min(ctx, start + PT);
+  // Which (sequence, query head) each column n stands for, the token range,
+  // and where the results go.
+  const int Gh = a.Hq / a.Hkv;            // query heads per KV head
+  int s, start, end, ctx;
+  PartRange pr{};
+  int col_seq = -1, col_head = -1;         // this lane's column
+  int slot = 0;
+  if constexpr (GROUP) {
+    const int32_t* it = a.items + static_cast<size_t>(blockIdx.y) * kItemInts;
+    s = it[0];
+    if (static_cast<unsigned>(s) >= static_cast<unsigned>(a.S)) return;
+    ctx = clamp_ctx(a, s, BS);
+    // rounded down like part_range: every tile starts where the loads assume
+    constexpr int kAlign = BS > kMTile ? BS : kMTile;
+    start = min(max(it[1], 0) / kAlign * kAlign, ctx);
+    end = min(max(it[2], start), ctx);
+    slot = it[3];
+    const int nmem = min(max(it[4], 0), kItemMembers);
+    const int mi = n / Gh;
+    if (mi < nmem) {
+      const int m = it[5 + mi];
+      if (static_cast<unsigned>(m) < static_cast<unsigned>(a.S)) {
+        col_seq = m;
+        col_head = g * Gh + n % Gh;
+      }
+    }
+  } else {
+    s = blockIdx.y;
+    ctx = clamp_ctx(a, s, BS);
+    pr = part_range(a, s, p, ctx, BS > kMTile ? BS : kMTile);
+    if (p >= pr.nparts) return;
+    start = pr.start;
+    end = pr.end;
+    if (n < kMG) {
+      col_seq = s;
+      col_head = g * kMG + n;
+    }
+  }
+  const int nparts = pr.nparts;
 
-  // B operand of S^T = K Q^T: lane (n, q) holds q[head n][32kk + 8q .. +8].
+  // B operand of S^T = K Q^T: lane (n, q) holds q[column n][32kk + 8q .. +8].
   u16x8_t qt[4];
   {
-    const T* qb = static_cast<const T*>(a.q) + (static_cast<size_t>(s) * a.Hq + g * kMG) * kMD;
+    const T* qb = static_cast<const T*>(a.q) +
+                  (static_cast<size_t>(max(col_seq, 0)) * a.Hq + max(col_head, 0)) * kMD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < kMG) v = *reinterpret_cast<const uint4*>(qb + n * kMD + 32 * kk + 8 * q);
+      if (col_seq >= 0) v = *reinterpret_cast<const uint4*>(qb + 32 * kk + 8 * q);
       qt[kk] = as_u16x8(v);
     }
   }
@@ -193,7 +233,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   // Fused step: the last partition owns position ctx-1.  In the tile that
   // holds it, the lanes of its row take the new K/V rows of head g from the
   // inputs instead of the pool and store them into the slot.
-  const bool append = a.new_key != nullptr && ctx > 0 && p == nparts - 1;
+  const bool append = !GROUP && a.new_key != nullptr && ctx > 0 && p == nparts - 1;
 
   // Issue every load of the tile at t0.  Each block's head tile is one buffer
   // resource; a row past the context, or in a block outside the pool, gets
@@ -350,10 +390,10 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   }
   __syncthreads();                         // every wavefront is done with its tile
 
-  // head n's sum over the four lane groups
+  // column n's sum over the four lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (n < kMG) {
+  if (n < NC) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -365,9 +405,22 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   }
   __syncthreads();
 
-  for (int i = tid; i < kMG * kMD; i += kMWaves * 64) {
+  for (int i = tid; i < NC * kMD; i += kMWaves * 64) {
     const int gi = i / kMD;
     const int d = i - gi * kMD;
+    // the column's sequence and query head (as the lanes of column gi had it)
+    int cs, ch;
+    if constexpr (GROUP) {
+      const int32_t* it = a.items + static_cast<size_t>(blockIdx.y) * kItemInts;
+      const int nmem = min(max(it[4], 0), kItemMembers);
+      const int mi = gi / Gh;
+      cs = mi < nmem ? it[5 + mi] : -1;
+      ch = g * Gh + gi % Gh;
+      if (static_cast<unsigned>(cs) >= static_cast<unsigned>(a.S)) continue;
+    } else {
+      cs = s;
+      ch = g * kMG + gi;
+    }
     float M = kNegInf;
 #pragma unroll
     for (int v = 0; v < kMWaves; ++v) M = fmaxf(M, red.m[v][gi]);
@@ -379,12 +432,13 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
       num = fmaf(red.o[v][gi][d], sw, num);
       den = fmaf(red.l[v][gi], sw, den);
     }
-    const int h = g * kMG + gi;
-    if (nparts == 1) {
-      static_cast<T*>(a.out)[(static_cast<size_t>(s) * a.Hq + h) * kMD + d] =
+    if (!GROUP && pr.total == 1) {
+      static_cast<T*>(a.out)[(static_cast<size_t>(cs) * a.Hq + ch) * kMD + d] =
           narrow<DT>(den > 0.f ? num / den : 0.f);
     } else {
-      const size_t idx = (static_cast<size_t>(s) * a.Hq + h) * a.pmax + p;
+      const int sl = GROUP ? slot : pr.slot;
+      if (static_cast<unsigned>(sl) >= static_cast<unsigned>(a.pmax)) continue;
+      const size_t idx = (static_cast<size_t>(cs) * a.Hq + ch) * a.pmax + sl;
       a.ws_o[idx * kMD + d] = num;
       if (d == 0) {
         a.ws_m[idx] = M;
@@ -394,16 +448,18 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   }
 }
 
-template <int DT>
+template <int DT, bool GROUP>
 int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
-  const dim3 grid(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
-                  static_cast<uint32_t>(a.pmax));
+  const dim3 grid(static_cast<uint32_t>(a.Hkv),
+                  static_cast<uint32_t>(GROUP ? a.n_items : a.S),
+                  static_cast<uint32_t>(GROUP ? 1 : a.grid_parts));
+  const dim3 block(kMWaves * 64);
   switch (bs) {
-    case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8>), grid, dim3(kMWaves * 64), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16>), grid, dim3(kMWaves * 64), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32>), grid, dim3(kMWaves * 64), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 64>), grid, dim3(kMWaves * 64), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 128>), grid, dim3(kMWaves * 64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8, GROUP>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16, GROUP>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32, GROUP>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 64, GROUP>), grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 128, GROUP>), grid, block, 0, st, a); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return launch_status();
@@ -413,8 +469,17 @@ int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
 
 int launch_decode_gqa_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st) {
   switch (dtype) {
-    case PA_BF16: return launch_bs<PA_BF16>(a, bs, st);
-    case PA_F16: return launch_bs<PA_F16>(a, bs, st);
+    case PA_BF16: return launch_bs<PA_BF16, false>(a, bs, st);
+    case PA_F16: return launch_bs<PA_F16, false>(a, bs, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+int launch_shared_prefix_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st) {
+  if (a.n_items <= 0) return PA_OK;
+  switch (dtype) {
+    case PA_BF16: return launch_bs<PA_BF16, true>(a, bs, st);
+    case PA_F16: return launch_bs<PA_F16, true>(a, bs, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }

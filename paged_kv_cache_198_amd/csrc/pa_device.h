@@ -121,11 +121,54 @@ struct DecodeArgs {
   // owns that position writes it into its slot and uses it from registers.
   const void* new_key;
   const void* new_value;
+  // Prefix sharing (pa_decode_cascade), null otherwise: sequence s's own
+  // tokens start at seq_start[s]; its partitions write workspace slots from
+  // slot_base[s] on, the slots below holding shared-prefix partials.
+  const int32_t* seq_start;
+  const int32_t* slot_base;
+  // Shared-prefix work items, kItemInts ints each (see pa_cascade_plan).
+  const int32_t* items;
+  int32_t n_items;
   int32_t S, Hq, Hkv, NB, MB, max_ctx;
   int32_t part_tokens;  // 0: one pass over the whole context
-  int32_t pmax;         // partitions per sequence in the grid / workspace
+  int32_t pmax;         // workspace slots per (sequence, query head)
+  int32_t grid_parts;   // partitions per sequence in the main grid
   float qscale;         // scale * log2(e)
 };
+
+// Shared-prefix work item: table row, token start, token end, workspace
+// slot, member count, then up to kItemMembers member rows (-1 = unused).
+constexpr int kItemMembers = 16;
+constexpr int kItemInts = 5 + kItemMembers;
+
+// Token range [start, end) and workspace slot of partition p of sequence s.
+// Plain decode: [p*PT, (p+1)*PT) clipped to ctx, slot p; a sequence that has
+// one partition is written straight to the output (total == 1), and one
+// with no tokens still gets a partition that writes zeros.  With prefix
+// sharing, partitions cover [seq_start[s], ctx) and use slots from
+// slot_base[s] on.
+struct PartRange {
+  int start, end, slot, nparts, total;
+};
+
+// `align` (a multiple of 32 and of bs) rounds seq_start down, so tiles and
+// row groups always start on the boundaries the kernels assume.
+__device__ __forceinline__ PartRange part_range(const DecodeArgs& a, int s, int p, int ctx,
+                                                int align) {
+  const int s0 = a.seq_start ? min(max(a.seq_start[s], 0) / align * align, ctx) : 0;
+  const int base = a.slot_base ? min(max(a.slot_base[s], 0), a.pmax) : 0;
+  const int len = ctx - s0;
+  const int PT = a.part_tokens > 0 ? a.part_tokens : max(len, 1);
+  int nparts = (len + PT - 1) / PT;
+  if (base == 0) nparts = max(nparts, 1);
+  PartRange r;
+  r.nparts = nparts;
+  r.total = min(base + nparts, a.pmax);   // never more slots than the workspace holds
+  r.start = s0 + p * PT;
+  r.end = min(ctx, r.start + PT);
+  r.slot = base + p;
+  return r;
+}
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s, int bs) {
   const int c = a.context_lens[s];
@@ -135,5 +178,8 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s, int bs) {
 // Launches the grouped-query MFMA main pass (bf16 / f16, D = 128, G = 8)
 // for the partitions in `a`; returns PA_ERR_UNSUPPORTED for other shapes.
 int launch_decode_gqa_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st);
+
+// Launches the shared-prefix pass over a.items (bf16 / f16, D = 128).
+int launch_shared_prefix_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st);
 
 }  // namespace pa

@@ -106,6 +106,27 @@ class PagedKV:
                           lens, mx, scale, partition_tokens, ws)
         return out
 
+    def step_cascade(self, query: torch.Tensor, seq_ids: Sequence[int], key: torch.Tensor,
+                     value: torch.Tensor, scale: float, partition_tokens: int = 0,
+                     prefix_tokens: int = 0, out: Optional[torch.Tensor] = None):
+        """``step`` with prefix sharing: blocks that forked sequences still
+        share are attended once per group (``pa_cascade_plan`` +
+        ``pa_decode_cascade``).  Returns (out, plan)."""
+        self.reserve(seq_ids)
+        MB = max(-(-self.alloc.seq_len(s) // self.bs) for s in seq_ids)
+        tables, lens = self.alloc.build_batch(list(seq_ids), max(MB, 1))
+        S, Hq = query.shape[0], query.shape[1]
+        plan = pa.pa_cascade_plan(tables, lens, self.bs, Hq, self.Hkv, partition_tokens,
+                                  prefix_tokens)
+        out = torch.empty_like(query) if out is None else out
+        ws = pa.make_cascade_workspace(S, Hq, self.D, plan, device=self.device)
+        pa.pa_decode_cascade(out, query, self.key_cache, self.value_cache,
+                             torch.from_numpy(tables).to(self.device),
+                             torch.from_numpy(lens).to(self.device), plan,
+                             int(lens.max()) if len(lens) else 1, scale, partition_tokens, ws,
+                             key=key, value=value)
+        return out, plan
+
     # -- accounting --------------------------------------------------------
     def used_blocks(self) -> int:
         return self.NB - self.alloc.num_free()

@@ -244,6 +244,77 @@ def make_shared_prefix(seed: int = 0, device="cpu", **over) -> SharedPrefixScrip
         step_k=sk, step_v=sv, q=q, key_cache=kc, value_cache=vc)
 
 
+# Forked batches (parallel sampling and beam search, page "PagedAttention: the
+# KV cache was the bottleneck all along", section "Virtual memory for
+# attention"): every sample of a prompt holds the prompt's full blocks in its
+# table; pairs of samples share a few more whole blocks (a later fork at a
+# block boundary, as beams do); the rest of each context is private.
+# Unforked sequences are mixed in, and the batch order is shuffled.
+FORKED = dict(prompts=4, samples=4, singles=3, Hq=32, Hkv=4, D=128, dtype="bf16", bs=16,
+              prompt_len=(100, 700), tail=(0, 300), pair_blocks=(0, 3), single_len=(1, 900),
+              slack_blocks=8)
+
+
+def make_forked(seed: int = 0, device="cpu", **over) -> DecodeWorkload:
+    """A decode workload whose block tables share physical blocks the way
+    forked sequences do; pool content as for :func:`make_decode`."""
+    cfg = dict(FORKED)
+    cfg.update(over)
+    rng = np.random.default_rng(seed)
+    bs, P, M = cfg["bs"], cfg["prompts"], cfg["samples"]
+    rows, lens = [], []
+    next_id = [0]
+
+    def fresh(n):
+        ids = list(range(next_id[0], next_id[0] + n))
+        next_id[0] += n
+        return ids
+
+    for _ in range(P):
+        plen = int(rng.integers(cfg["prompt_len"][0], cfg["prompt_len"][1] + 1))
+        prompt = fresh(plen // bs)
+        pair = []
+        for j in range(M):
+            if j % 2 == 0:
+                pair = fresh(int(rng.integers(cfg["pair_blocks"][0], cfg["pair_blocks"][1] + 1)))
+            shared = prompt + pair
+            ctx = plen + int(rng.integers(cfg["tail"][0], cfg["tail"][1] + 1)) + 1
+            ctx = max(ctx, len(shared) * bs + 1)          # shared blocks lie before ctx-1
+            rows.append(shared + fresh(-(-ctx // bs) - len(shared)))
+            lens.append(ctx)
+    for _ in range(cfg["singles"]):
+        ctx = int(rng.integers(cfg["single_len"][0], cfg["single_len"][1] + 1))
+        rows.append(fresh(-(-ctx // bs)))
+        lens.append(ctx)
+    S = len(rows)
+    order = rng.permutation(S)
+    NB = next_id[0] + cfg["slack_blocks"]
+    perm = rng.permutation(NB).astype(np.int32)            # logical id -> physical block
+    MB = max(len(r) for r in rows)
+    tables = np.full((S, MB), -1, dtype=np.int32)
+    ctx_lens = np.zeros(S, dtype=np.int32)
+    for dst, src in enumerate(order):
+        tables[dst, :len(rows[src])] = perm[rows[src]]
+        ctx_lens[dst] = lens[src]
+    mask = filled_mask(tables, np.maximum(ctx_lens.astype(np.int64) - 1, 0), bs, NB)
+    gen = _generator(seed, device)
+    dt, Hq, Hkv, D = cfg["dtype"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    q = _randn((S, Hq, D), gen, device, dt)
+    pools = []
+    poison = ~torch.from_numpy(mask).to(device)[:, None, :, None]
+    for _ in range(2):
+        p = torch.randn(NB, Hkv, bs, D, generator=gen, device=device, dtype=torch.float32)
+        p.masked_fill_(poison, float("nan"))
+        pools.append(p.to(KV_DTYPES[dt]))
+    nk = _randn((S, Hkv, D), gen, device, dt)
+    nv = _randn((S, Hkv, D), gen, device, dt)
+    return DecodeWorkload(
+        name="forked", seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
+        scale=float(np.float32(1.0 / np.sqrt(D))), partition_tokens=0,
+        context_lens=ctx_lens, block_tables=tables, block_order=perm, q=q,
+        key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     """Host copy of a KV-dtype tensor as its raw storage: float32 / float16 as
     themselves, bfloat16 as its uint16 bit patterns (numpy has no bfloat16)."""
