@@ -171,19 +171,21 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
  * merged by the partition reduce.
  *
  * pa_cascade_plan (host only, no device call) reads the batch's block tables
- * and context lengths and builds the plan:
+ * and context lengths and builds the plan, a list of work items:
  *   * sequences whose tables start with the same physical block form a
- *     group, taken in chunks of 16 / (Hq / Hkv) members (the query heads of
- *     one chunk fill the 16 columns of one matrix-core tile);
+ *     group, sorted by table row and taken in chunks of 16 / (Hq / Hkv)
+ *     members (the query heads of one chunk fill the 16 columns of one
+ *     matrix-core tile);
  *   * a chunk's shared prefix T_sh is the run of leading table entries that
  *     all its members hold, counting only blocks that lie wholly before
  *     each member's last position, rounded down to a multiple of
- *     max(bs, 32) tokens; chunks with T_sh = 0 and sequences in no chunk
- *     are planned as in a plain decode;
- *   * the prefix is cut into pieces of prefix_tokens tokens (a multiple of
- *     max(bs, 32); 0 = one piece), one work item each;
- *   * each sequence's suffix [T_sh, ctx) is cut into partitions of
- *     partition_tokens tokens (a multiple of bs; 0 = one partition).
+ *     max(bs, 32) tokens; it is cut into pieces of prefix_tokens tokens (a
+ *     multiple of max(bs, 32); 0 = one piece), one item each, whose members
+ *     are the chunk;
+ *   * each sequence's suffix [T_sh, ctx) (the whole context when it is in
+ *     no chunk) is cut into partitions of partition_tokens tokens (a
+ *     multiple of bs; 0 = one partition), one single-member item each;
+ *   * items are ordered longest first.
  * Inputs:
  *   block_tables     host int32 [S][MB], as for pa_decode_attention.
  *   context_lens     host int32 [S] (clamped to [0, MB*bs]).
@@ -192,14 +194,14 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
  *                    0), slot_base[S] (prefix pieces before the suffix
  *                    partitions), then n_items work items of
  *                    PA_CASCADE_ITEM_INTS ints: table sequence, token start,
- *                    token end, partial slot, member count, 16 member
+ *                    token end, partial slot (-1: the sequence's only piece,
+ *                    written to `out` directly), member count, 16 member
  *                    sequences (unused ones -1).
  *   info             host int32 [PA_CASCADE_INFO_INTS]: n_items, slots_max
- *                    (partial slots per sequence and head), suffix_parts
- *                    (most suffix partitions of any sequence), plan ints
- *                    needed, prefix rows read by the group pass, rows the
- *                    members would have read on top of that in a plain
- *                    decode.
+ *                    (partial slots per sequence and head), the most suffix
+ *                    partitions of any sequence, plan ints needed, prefix
+ *                    rows read by the group items, rows the members would
+ *                    have read on top of that in a plain decode.
  * Returns PA_ERR_WORKSPACE (with info filled in) when plan is NULL or
  * shorter than info[3]; call again with a plan that large. */
 #define PA_CASCADE_ITEM_INTS 21
@@ -215,28 +217,28 @@ size_t pa_cascade_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t slot
 
 /* Decode attention (and, when key / value are given, the fused store of the
  * new token as in pa_decode_step) following a plan from pa_cascade_plan.
- * Up to three launches on `stream`: the prefix pass (matrix cores, one
- * workgroup per work item and KV head), the suffix pass (the same kernels as
- * pa_decode_attention, starting at seq_start), and the partition reduce.
+ * Two launches on `stream`: every work item (matrix cores, one workgroup per
+ * item and KV head), then the partition reduce when slots_max > 1.
  *   plan             device int32 copy of the plan's first
  *                    2*S + n_items*PA_CASCADE_ITEM_INTS ints.
  *   n_items,
- *   slots_max,
- *   suffix_parts     info[0..2] of the plan.
+ *   slots_max        info[0..1] of the plan.
  *   key, value       device [S][Hkv][D] new rows, or both NULL for
- *                    attention only.
+ *                    attention only; the row is stored by the item that
+ *                    ends at the sequence's last position.
+ *   partition_tokens as given to pa_cascade_plan.
  *   workspace        device, pa_cascade_workspace_bytes(...) bytes,
- *                    256-byte aligned.
- * The plan must have been built from the same block tables and lengths:
- * entries are bounds-checked on the device (a bad plan gives wrong numbers,
- * never an access outside the pools or the workspace) but not validated.
- * Supported: f16 / bf16, D = 128, Hq / Hkv in {1, 2, 4, 8}, bs as for
- * pa_decode_attention; every other argument as there. */
+ *                    256-byte aligned; may be NULL when that size is 0.
+ * The plan must have been built from the same block tables, lengths and
+ * partition_tokens: entries are bounds-checked on the device (a bad plan
+ * gives wrong numbers, never an access outside the pools or the workspace)
+ * but not validated.  Supported: f16 / bf16, D = 128, Hq / Hkv in
+ * {1, 2, 4, 8}, bs as for pa_decode_attention; every other argument as
+ * there. */
 int pa_decode_cascade(void* out, const void* query, const void* key, const void* value,
                       void* key_cache, void* value_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* plan, int32_t n_items, int32_t slots_max,
-                      int32_t suffix_parts,
                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                       int32_t bs, int32_t NB, int32_t MB,
                       int32_t max_context_len, float scale,

@@ -54,8 +54,8 @@ _SIGNATURES = {
     "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_cascade": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                   _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t,
-                                   _c_i32, _c_p]),
+                                   _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t, _c_i32,
+                                   _c_p]),
     "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
                                 _c_i32, _c_i32, _c_i64, _c_p]),
     "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
@@ -259,7 +259,9 @@ CASCADE_INFO_INTS = 6
 
 class CascadePlan:
     """A plan from ``pa_cascade_plan``: ``plan`` (host int32: seq_start[S],
-    slot_base[S], then n_items work items of 21 ints) and its sizes."""
+    slot_base[S], then n_items work items of 21 ints: table sequence, token
+    start, token end, slot (-1 = direct output), member count, members) and
+    its sizes."""
 
     def __init__(self, S: int, plan: np.ndarray, info: np.ndarray):
         self.S = S
@@ -360,7 +362,7 @@ def pa_decode_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
         _dev(out, "out"), _dev(query, "query"), kp, vp, _dev(key_cache, "key_cache"),
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
         _dev(context_lens, "context_lens", torch.int32), _dev(pd, "plan", torch.int32),
-        plan.n_items, plan.slots_max, plan.suffix_parts, S, Hq, Hkv, D, bs, NB, MB,
+        plan.n_items, plan.slots_max, S, Hq, Hkv, D, bs, NB, MB,
         int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
         _stream(stream))
     _check(rc, "pa_decode_cascade")

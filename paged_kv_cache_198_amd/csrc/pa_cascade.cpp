@@ -10,10 +10,12 @@
 //   * a shared prefix [0, T_sh), attended once per group by the matrix-core
 //     kernel with the members' queries as the tile's columns, and
 //   * its own suffix [T_sh, ctx), attended per sequence as in a plain decode.
-// Each piece leaves a partial softmax state (max, sum, unnormalised output)
-// in the workspace; the partition reduce combines them, which is exact
-// because softmax over a union of disjoint token sets is the weighted merge
-// of the per-set results.
+// Both kinds of piece are work items of one launch: a prefix item lists the
+// group's members, a suffix item its one sequence.  Each piece leaves a
+// partial softmax state (max, sum, unnormalised output) in the workspace; the
+// partition reduce combines them, which is exact because softmax over a
+// union of disjoint token sets is the weighted merge of the per-set results.
+// A sequence that is a single piece writes its output directly.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -120,18 +122,52 @@ extern "C" int pa_cascade_plan(const int32_t* block_tables, const int32_t* conte
     }
   }
 
-  // Suffix partitions and the partial slots each sequence needs.
+  // Suffix partitions: one single-member item each, in slots base..; a
+  // sequence with one piece in all writes its output directly (slot -1).
+  struct Suffix {
+    int32_t s, t0, t1, slot;
+  };
+  std::vector<Suffix> suffix;
   int32_t suffix_parts = 1, slots_max = 1;
   for (int s = 0; s < S; ++s) {
-    const int64_t ctx = std::min<int64_t>(std::max(context_lens[s], 0), int64_t(MB) * bs);
-    const int64_t len = ctx - start[s];
-    int64_t np = partition_tokens > 0 ? (len + partition_tokens - 1) / partition_tokens
+    const int32_t ctx = static_cast<int32_t>(
+        std::min<int64_t>(std::max(context_lens[s], 0), int64_t(MB) * bs));
+    const int32_t len = ctx - start[s];
+    int32_t np = partition_tokens > 0 ? (len + partition_tokens - 1) / partition_tokens
                                       : (len > 0 ? 1 : 0);
-    if (base[s] == 0) np = std::max<int64_t>(np, 1);
-    suffix_parts = static_cast<int32_t>(std::max<int64_t>(suffix_parts, np));
-    slots_max = static_cast<int32_t>(std::max<int64_t>(slots_max, base[s] + np));
+    if (base[s] == 0) np = std::max(np, 1);
+    suffix_parts = std::max(suffix_parts, np);
+    slots_max = std::max(slots_max, base[s] + np);
+    const int32_t PT = partition_tokens > 0 ? partition_tokens : std::max(len, 1);
+    const bool direct = base[s] + np == 1;
+    for (int32_t p = 0; p < np; ++p) {
+      const int32_t t0 = start[s] + p * PT;
+      suffix.push_back({s, t0, std::min(ctx, t0 + PT), direct ? -1 : base[s] + p});
+    }
   }
-  const int32_t n_items = static_cast<int32_t>(items.size() / kItemInts);
+  for (const Suffix& x : suffix) {
+    const size_t at = items.size();
+    items.resize(at + kItemInts, -1);
+    items[at + 0] = x.s;
+    items[at + 1] = x.t0;
+    items[at + 2] = x.t1;
+    items[at + 3] = x.slot;
+    items[at + 4] = 1;
+    items[at + 5] = x.s;
+  }
+  // Longest first: the hardware hands out workgroups roughly in grid order,
+  // so long items start first and short ones fill the tail.
+  const size_t n_all = items.size() / kItemInts;
+  std::vector<size_t> order(n_all);
+  for (size_t i = 0; i < n_all; ++i) order[i] = i;
+  auto rows = [&](size_t i) { return items[i * kItemInts + 2] - items[i * kItemInts + 1]; };
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t x, size_t y) { return rows(x) > rows(y); });
+  std::vector<int32_t> sorted(items.size());
+  for (size_t i = 0; i < n_all; ++i)
+    std::copy_n(items.begin() + order[i] * kItemInts, kItemInts, sorted.begin() + i * kItemInts);
+  items.swap(sorted);
+  const int32_t n_items = static_cast<int32_t>(n_all);
   const size_t need = 2 * static_cast<size_t>(S) + items.size();
   info[0] = n_items;
   info[1] = slots_max;

@@ -427,7 +427,7 @@ namespace {
 // host-side sizes.
 struct Cascade {
   const int32_t* plan;
-  int32_t n_items, slots_max, suffix_parts;
+  int32_t n_items, slots_max;
 };
 
 int decode_impl(void* out, const void* query, const void* new_key, const void* new_value,
@@ -463,12 +463,10 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
     // the prefix pass runs on the matrix cores only
     if ((dtype != PA_BF16 && dtype != PA_F16) || D != 128) return PA_ERR_UNSUPPORTED;
     if (!cas->plan || (reinterpret_cast<uintptr_t>(cas->plan) & 3u)) return PA_ERR_INVALID;
-    if (cas->n_items < 0 || cas->slots_max < 1 || cas->suffix_parts < 1 ||
-        cas->suffix_parts > cas->slots_max || (cas->n_items > 0 && cas->slots_max < 2))
-      return PA_ERR_INVALID;
+    if (cas->n_items < 0 || cas->slots_max < 1) return PA_ERR_INVALID;
     if (cas->n_items > 65535) return PA_ERR_UNSUPPORTED;
     pmax = cas->slots_max;
-    grid_parts = cas->suffix_parts;
+    grid_parts = 1;
   }
   if (S > 65535 || pmax > 65535) return PA_ERR_UNSUPPORTED;
 
@@ -513,10 +511,10 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
   // other shape runs the vector-ALU kernel.
   const bool mfma = (dtype == PA_BF16 || dtype == PA_F16) && D == 128 && G == 8 &&
                     a.part_tokens % 32 == 0;
-  int rc = PA_OK;
-  if (cas) rc = pa::launch_shared_prefix_mfma(a, dtype, bs, st);
-  if (rc != PA_OK) return rc;
-  if (mfma) {
+  int rc;
+  if (cas) {
+    rc = pa::launch_items_mfma(a, dtype, bs, st);
+  } else if (mfma) {
     rc = pa::launch_decode_gqa_mfma(a, dtype, bs, st);
   } else {
     switch (dtype) {
@@ -566,14 +564,14 @@ extern "C" int pa_decode_cascade(void* out, const void* query, const void* key,
                                  const void* value, void* key_cache, void* value_cache,
                                  const int32_t* block_tables, const int32_t* context_lens,
                                  const int32_t* plan, int32_t n_items, int32_t slots_max,
-                                 int32_t suffix_parts, int32_t S, int32_t Hq, int32_t Hkv,
+                                 int32_t S, int32_t Hq, int32_t Hkv,
                                  int32_t D, int32_t bs, int32_t NB, int32_t MB,
                                  int32_t max_context_len, float scale, int32_t partition_tokens,
                                  void* workspace, size_t workspace_bytes, int32_t dtype,
                                  void* stream) {
   if ((key == nullptr) != (value == nullptr)) return PA_ERR_INVALID;
   if (key && (!pa::aligned16(key) || !pa::aligned16(value))) return PA_ERR_INVALID;
-  const pa::Cascade cas{plan, n_items, slots_max, suffix_parts};
+  const pa::Cascade cas{plan, n_items, slots_max};
   return pa::decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
                          context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
                          partition_tokens, workspace, workspace_bytes, dtype, stream, &cas);

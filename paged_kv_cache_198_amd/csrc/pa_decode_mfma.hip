@@ -128,10 +128,11 @@ struct TileRegs {
 
 // GROUP = false: grouped-query decode, the 8 query heads of KV head g of
 // sequence s are the tile's columns; grid (Hkv, S, partitions).
-// GROUP = true: shared-prefix pass, one work item per grid row; the columns
-// are (member sequence, query head) pairs of sequences whose block tables
-// share the item's token range, which is read once for all of them; every
-// column writes a partial to its member's workspace slot.
+// GROUP = true: work items, one per grid row.  A shared-prefix item's
+// columns are (member sequence, query head) pairs of sequences whose block
+// tables share the item's token range, which is read once for all of them;
+// a suffix item has one member, the sequence itself.  Each column writes a
+// partial to its member's workspace slot, or, for slot -1, the final output.
 template <int DT, int BS, bool GROUP>
 __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
@@ -170,17 +171,20 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   PartRange pr{};
   int col_seq = -1, col_head = -1;         // this lane's column
   int slot = 0;
+  bool owns_last = false;                  // the item ends at its sequence's last token
   if constexpr (GROUP) {
     const int32_t* it = a.items + static_cast<size_t>(blockIdx.y) * kItemInts;
     s = it[0];
     if (static_cast<unsigned>(s) >= static_cast<unsigned>(a.S)) return;
     ctx = clamp_ctx(a, s, BS);
-    // rounded down like part_range: every tile starts where the loads assume
-    constexpr int kAlign = BS > kMTile ? BS : kMTile;
+    // Rounded down to where tiles may start: anywhere on a block boundary
+    // when bs <= 32, at a 32-row offset inside a block otherwise.
+    constexpr int kAlign = BS < kMTile ? BS : kMTile;
     start = min(max(it[1], 0) / kAlign * kAlign, ctx);
     end = min(max(it[2], start), ctx);
     slot = it[3];
     const int nmem = min(max(it[4], 0), kItemMembers);
+    owns_last = nmem == 1 && it[5] == s && end == ctx;
     const int mi = n / Gh;
     if (mi < nmem) {
       const int m = it[5 + mi];
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   // Fused step: the last partition owns position ctx-1.  In the tile that
   // holds it, the lanes of its row take the new K/V rows of head g from the
   // inputs instead of the pool and store them into the slot.
-  const bool append = !GROUP && a.new_key != nullptr && ctx > 0 && p == nparts - 1;
+  const bool append = a.new_key != nullptr && ctx > 0 && (GROUP ? owns_last : p == nparts - 1);
 
   // Issue every load of the tile at t0.  Each block's head tile is one buffer
   // resource; a row past the context, or in a block outside the pool, gets
@@ -432,12 +436,13 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
       num = fmaf(red.o[v][gi][d], sw, num);
       den = fmaf(red.l[v][gi], sw, den);
     }
-    if (!GROUP && pr.total == 1) {
+    if (GROUP ? slot < 0 : pr.total == 1) {
       static_cast<T*>(a.out)[(static_cast<size_t>(cs) * a.Hq + ch) * kMD + d] =
           narrow<DT>(den > 0.f ? num / den : 0.f);
     } else {
       const int sl = GROUP ? slot : pr.slot;
-      if (static_cast<unsigned>(sl) >= static_cast<unsigned>(a.pmax)) continue;
+      // no workspace exists when pmax < 2
+      if (a.pmax < 2 || static_cast<unsigned>(sl) >= static_cast<unsigned>(a.pmax)) continue;
       const size_t idx = (static_cast<size_t>(cs) * a.Hq + ch) * a.pmax + sl;
       a.ws_o[idx * kMD + d] = num;
       if (d == 0) {
@@ -475,7 +480,7 @@ int launch_decode_gqa_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipSt
   }
 }
 
-int launch_shared_prefix_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st) {
+int launch_items_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st) {
   if (a.n_items <= 0) return PA_OK;
   switch (dtype) {
     case PA_BF16: return launch_bs<PA_BF16, true>(a, bs, st);

@@ -179,7 +179,7 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int s, int bs) {
 // for the partitions in `a`; returns PA_ERR_UNSUPPORTED for other shapes.
 int launch_decode_gqa_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st);
 
-// Launches the shared-prefix pass over a.items (bf16 / f16, D = 128).
-int launch_shared_prefix_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st);
+// Launches the work items in a.items (bf16 / f16, D = 128).
+int launch_items_mfma(const DecodeArgs& a, int32_t dtype, int32_t bs, hipStream_t st);
 
 }  // namespace pa

@@ -91,13 +91,13 @@ def test_workspace_size():
 
 def cascade_call(**over):
     a = dict(out=FAKE, q=FAKE, k=None, v=None, kc=FAKE, vc=FAKE, tables=FAKE, ctx=FAKE,
-             plan=FAKE, n_items=2, slots_max=3, parts=1, S=2, Hq=8, Hkv=1, D=128, bs=16, NB=10,
+             plan=FAKE, n_items=2, slots_max=3, S=2, Hq=8, Hkv=1, D=128, bs=16, NB=10,
              MB=4, max_ctx=64, scale=0.1, part=0, ws=FAKE + 256, ws_bytes=1 << 20,
              dtype=pa.PA_BF16)
     a.update(over)
     return pa.lib().pa_decode_cascade(
         a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"], a["tables"], a["ctx"], a["plan"],
-        a["n_items"], a["slots_max"], a["parts"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+        a["n_items"], a["slots_max"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
         a["NB"], a["MB"], a["max_ctx"], a["scale"], a["part"], a["ws"], a["ws_bytes"], a["dtype"],
         None)
 
@@ -110,9 +110,9 @@ def cascade_call(**over):
     (dict(plan=None), pa.PA_ERR_INVALID),
     (dict(plan=FAKE + 2), pa.PA_ERR_INVALID),
     (dict(n_items=-1), pa.PA_ERR_INVALID),
-    (dict(slots_max=1), pa.PA_ERR_INVALID),              # items need prefix slots
-    (dict(parts=4), pa.PA_ERR_INVALID),                  # more suffix parts than slots
-    (dict(n_items=70000, slots_max=70000), pa.PA_ERR_UNSUPPORTED),
+    (dict(slots_max=0), pa.PA_ERR_INVALID),
+    (dict(n_items=70000), pa.PA_ERR_UNSUPPORTED),
+    (dict(slots_max=70000), pa.PA_ERR_UNSUPPORTED),
     (dict(ws=None), pa.PA_ERR_WORKSPACE),
     (dict(ws_bytes=100), pa.PA_ERR_WORKSPACE),
     (dict(part=24), pa.PA_ERR_INVALID),

@@ -19,37 +19,45 @@ def clamp_ctx(w, s):
 
 
 def check_plan(tables, lens, bs, G, part, pfx, plan):
+    """Every invariant of a plan; returns each sequence's pieces as
+    (t0, t1, slot) in token order."""
     S = tables.shape[0]
     align = max(bs, 32)
     per_item = 16 // G
     start, base, items = plan.seq_start, plan.slot_base, plan.items
     assert items.shape == (plan.n_items, ITEM)
-    pieces = {s: [] for s in range(S)}
-    seen = set()
+    rows = items[:, 2] - items[:, 1]
+    assert (np.diff(rows) <= 0).all()                    # longest first
+    prefix = {s: [] for s in range(S)}
+    suffix = {s: [] for s in range(S)}
+    chunks = []
     for it in items:
         t, t0, t1, slot, nmem = (int(x) for x in it[:5])
         members = [int(m) for m in it[5:5 + nmem]]
-        assert 2 <= nmem <= per_item
+        assert 1 <= nmem <= per_item
         assert all(int(m) == -1 for m in it[5 + nmem:])
         assert t in members and len(set(members)) == nmem
-        assert 0 <= t0 < t1 and t0 % align == 0
+        if nmem == 1:                                    # a sequence's own partition
+            suffix[t].append((t0, t1, slot))
+            continue
+        assert 0 <= t0 < t1 and t0 % align == 0 and slot >= 0
         if pfx:
             assert t1 - t0 <= pfx
         for m in members:
             nblk = -(-t1 // bs)
             # the item reads member m's tokens [t0, t1) through table row t
             assert np.array_equal(tables[m, :nblk], tables[t, :nblk])
-            pieces[m].append((t0, t1, slot))
-        key = tuple(members)
-        seen.add(key)
-    # each sequence is in at most one chunk
-    flat = [m for key in seen for m in key]
-    assert len(flat) == len(set(flat))
+            prefix[m].append((t0, t1, slot))
+        if tuple(members) not in chunks:
+            chunks.append(tuple(members))
+    flat = [m for c in chunks for m in c]
+    assert len(flat) == len(set(flat))                   # at most one chunk per sequence
     parts_max, slots_max, saved = 1, 1, 0
+    pieces = {}
     for s in range(S):
         ctx = max(0, min(int(lens[s]), tables.shape[1] * bs))
         full = (ctx - 1) // bs if ctx > 0 else 0
-        ps = sorted(pieces[s])
+        ps = sorted(prefix[s])
         assert start[s] % align == 0 and start[s] <= full * bs
         assert base[s] == len(ps)
         # prefix pieces tile [0, start) with slots 0..k-1 in order
@@ -58,15 +66,29 @@ def check_plan(tables, lens, bs, G, part, pfx, plan):
             assert (t0, slot) == (pos, i)
             pos = t1
         assert pos == start[s]
+        # suffix partitions tile [start, ctx) in slots base.., or one direct piece
         n = ctx - start[s]
         np_ = -(-n // part) if part else (1 if n > 0 else 0)
         if base[s] == 0:
             np_ = max(np_, 1)
+        ss = sorted(suffix[s])
+        assert len(ss) == np_
+        P = part or max(n, 1)
+        direct = base[s] + np_ == 1
+        for p, (t0, t1, slot) in enumerate(ss):
+            assert (t0, t1) == (start[s] + p * P, min(ctx, start[s] + (p + 1) * P))
+            assert slot == (-1 if direct else base[s] + p)
         parts_max, slots_max = max(parts_max, np_), max(slots_max, base[s] + np_)
+        pieces[s] = ps + ss
     for it in items:
         saved += (int(it[2]) - int(it[1])) * (int(it[4]) - 1)
     assert (plan.suffix_parts, plan.slots_max, plan.saved_rows) == (parts_max, slots_max, saved)
+    assert plan.prefix_rows == int(sum(r for r, it in zip(rows, items) if it[4] > 1))
     return pieces
+
+
+def n_prefix_items(plan):
+    return int((plan.items[:, 4] > 1).sum())
 
 
 def group_lcp_tokens(tables, lens, bs, members):
@@ -91,7 +113,7 @@ def test_plan_invariants(G, bs, dtype, part, pfx, seed):
     w = synth.make_forked(seed, Hq=4 * G, Hkv=4, D=16, bs=bs, dtype=dtype)
     plan = pa.pa_cascade_plan(w.block_tables, w.context_lens, bs, w.Hq, w.Hkv, part, pfx)
     check_plan(w.block_tables, w.context_lens, bs, G, part, pfx, plan)
-    assert plan.n_items > 0
+    assert n_prefix_items(plan) > 0
     # every sequence whose first block is shared gets at least the common
     # prefix of its whole group when the group fits one tile
     align = max(bs, 32)
@@ -115,23 +137,44 @@ def test_hand_worked_plan():
     lens = np.array([40, 47, 64, 33, 50], dtype=np.int32)
     plan = pa.pa_cascade_plan(tables, lens, 16, 8, 8)             # G = 1: one chunk
     # the chunk of all four sharers has a 16-token common prefix, which the
-    # 32-token alignment rounds to nothing
-    assert plan.n_items == 0 and not plan.seq_start.any() and plan.slots_max == 1
+    # 32-token alignment rounds to nothing: one direct item per sequence
+    assert n_prefix_items(plan) == 0 and not plan.seq_start.any() and plan.slots_max == 1
+    assert sorted(plan.items[:, :6].tolist()) == [[0, 0, 40, -1, 1, 0], [1, 0, 47, -1, 1, 1],
+                                                  [2, 0, 64, -1, 1, 2], [3, 0, 33, -1, 1, 3],
+                                                  [4, 0, 50, -1, 1, 4]]
     plan = pa.pa_cascade_plan(tables, lens, 16, 64, 8)            # G = 8: pairs
     # sorted by row (an extension before its prefix): 4 [5,6,7] | 0 [5,6] |
-    # 1 [5,6] | 2 [5,9,10] -> pairs (4, 0) sharing 32 tokens, (1, 2) sharing 16
-    assert plan.n_items == 1
-    assert plan.items[0, :7].tolist() == [4, 0, 32, 0, 2, 4, 0]
+    # 1 [5,6] | 2 [5,9,10] -> pairs (4, 0) sharing 32 tokens, (1, 2) sharing 16;
+    # items longest first (stable): 2, 1, 3, the prefix, 4's suffix, 0's suffix
+    assert plan.items[:, :7].tolist() == [
+        [2, 0, 64, -1, 1, 2, -1], [1, 0, 47, -1, 1, 1, -1], [3, 0, 33, -1, 1, 3, -1],
+        [4, 0, 32, 0, 2, 4, 0], [4, 32, 50, 1, 1, 4, -1], [0, 32, 40, 1, 1, 0, -1]]
     assert plan.seq_start.tolist() == [32, 0, 0, 0, 32]
     assert plan.slot_base.tolist() == [1, 0, 0, 0, 1]
     assert (plan.slots_max, plan.suffix_parts, plan.prefix_rows, plan.saved_rows) == (2, 1, 32, 32)
+    # with 16-token partitions the suffixes split, and every piece uses a slot
+    plan = pa.pa_cascade_plan(tables, lens, 16, 64, 8, partition_tokens=16)
+    check_plan(tables, lens, 16, 8, 16, 0, plan)
+    assert plan.slots_max == 4 and plan.suffix_parts == 4          # row 2: 64 tokens
+    assert sorted(plan.items[plan.items[:, 0] == 4][:, :4].tolist()) == [
+        [4, 0, 32, 0], [4, 32, 48, 1], [4, 48, 50, 2]]
 
 
 def test_no_sharing_plans_a_plain_decode():
     w = synth.make_decode("tiny", device="cpu")
     plan = pa.pa_cascade_plan(w.block_tables, w.context_lens, w.bs, w.Hq, w.Hkv, 32)
-    assert plan.n_items == 0 and not plan.seq_start.any() and not plan.slot_base.any()
+    check_plan(w.block_tables, w.context_lens, w.bs, 1, 32, 0, plan)
+    assert n_prefix_items(plan) == 0 and not plan.seq_start.any() and not plan.slot_base.any()
     assert plan.suffix_parts == -(-int(w.context_lens.max()) // 32)
+    assert plan.n_items == int(sum(max(1, -(-int(c) // 32)) for c in w.context_lens))
+
+
+def test_empty_and_single_token_sequences():
+    tables = np.array([[0, 1], [2, -1], [-1, -1]], dtype=np.int32)
+    plan = pa.pa_cascade_plan(tables, np.array([20, 1, 0], dtype=np.int32), 16, 4, 4, 16)
+    check_plan(tables, np.array([20, 1, 0]), 16, 1, 16, 0, plan)
+    assert sorted(plan.items[:, :4].tolist()) == [[0, 0, 16, 0], [0, 16, 20, 1],
+                                                  [1, 0, 1, -1], [2, 0, 0, -1]]
 
 
 def test_newest_block_is_never_shared():
@@ -143,7 +186,7 @@ def test_newest_block_is_never_shared():
     plan = pa.pa_cascade_plan(tables, np.array([33, 48], dtype=np.int32), 16, 1, 1)
     assert plan.seq_start.tolist() == [32, 32]
     plan = pa.pa_cascade_plan(tables, np.array([32, 48], dtype=np.int32), 16, 1, 1)
-    assert plan.n_items == 0
+    assert n_prefix_items(plan) == 0
 
 
 @pytest.mark.parametrize("kw", [dict(bs=24), dict(Hq=12), dict(Hq=64, Hkv=4),
@@ -169,27 +212,23 @@ def partial_state(q, K, V, scale):
 def test_planned_pieces_merge_to_the_decode(G, bs, part, pfx):
     w = synth.make_forked(3, Hq=2 * G, Hkv=2, D=16, bs=bs, dtype="f32", prompts=3, samples=4,
                           prompt_len=(40, 300), tail=(0, 90), single_len=(1, 200))
-    plan = pa.pa_cascade_plan(w.block_tables, w.context_lens, bs, w.Hq, w.Hkv, part, pfx)
-    pieces = check_plan(w.block_tables, w.context_lens, bs, G, part, pfx, plan)
+    lens = np.maximum(w.context_lens - 1, 0).astype(np.int32)   # the pre-step pool holds ctx-1
+    plan = pa.pa_cascade_plan(w.block_tables, lens, bs, w.Hq, w.Hkv, part, pfx)
+    pieces = check_plan(w.block_tables, lens, bs, G, part, pfx, plan)
+    assert n_prefix_items(plan) > 0
     q = w.q.numpy().astype(np.float64)
     kc, vc = w.key_cache.numpy(), w.value_cache.numpy()
-    lens_filled = np.maximum(w.context_lens - 1, 0)     # the pre-step pool holds ctx-1 tokens
-    ref = od.paged_decode(w.q.numpy(), w.key_cache.numpy(), w.value_cache.numpy(),
-                          w.block_tables, lens_filled, w.scale, "f32")
+    live = [s for s in range(w.S) if lens[s] > 0]
+    ref = od.paged_decode(w.q.numpy(), kc, vc, w.block_tables, lens, w.scale, "f32", seqs=live)
     Gh = w.Hq // w.Hkv
-    for s in range(w.S):
-        n = int(lens_filled[s])
-        if n == 0:
-            continue
+    for i, s in enumerate(live):
+        n = int(lens[s])
         K, V = od.gather_sequence(kc, vc, w.block_tables[s], n, bs, "f32")
-        st = int(plan.seq_start[s])
         cuts = [(t0, t1) for t0, t1, _ in pieces[s]]
-        P = part or max(n - st, 1)
-        cuts += [(a, min(n, a + P)) for a in range(st, n, P)]
         for h in range(w.Hq):
             states = [partial_state(q[s, h], K[a:b, h // Gh], V[a:b, h // Gh], w.scale)
                       for a, b in cuts if b > a]
             M = max(m for m, _, _ in states)
             num = sum(np.exp(m - M) * o for m, _, o in states)
             den = sum(np.exp(m - M) * l for m, l, _ in states)
-            assert np.allclose(num / den, ref[s, h], rtol=0, atol=1e-12)
+            assert np.allclose(num / den, ref[i, h], rtol=0, atol=1e-12)

@@ -637,7 +637,7 @@ def test_cascade_decode(G, Hkv, bs, dtype, part, pfx):
          f"S={w.S} max_ctx={w.max_context_len}")
     lens = np.maximum(w.context_lens - 1, 0).astype(np.int32)   # the pool holds ctx-1 tokens
     out, kc, vc, plan = run_cascade(w, lens, part, pfx, fused=False)
-    assert plan.n_items > 0
+    assert (plan.items[:, 4] > 1).any()                     # some prefix is shared
     live = [s for s in range(w.S) if lens[s] > 0]
     ref, _ = oracle_step(w, live, lens=lens, write=False)
     got = widened(out, w.dtype)
@@ -656,7 +656,7 @@ def test_cascade_step(G, Hkv, bs, dtype, part, pfx):
     note(f"case cascade step G={G} Hkv={Hkv} bs={bs} {dtype} part={part} prefix={pfx} "
          f"S={w.S} max_ctx={w.max_context_len}")
     out, kc, vc, plan = run_cascade(w, w.context_lens, part, pfx, fused=True)
-    assert plan.n_items > 0
+    assert (plan.items[:, 4] > 1).any()
     ref, slots = oracle_step(w)
     err = float(np.max(np.abs(widened(out, w.dtype) - ref)))
     note(f"  max abs err {err:.3e} (bound {TOL[w.dtype]:g})")
@@ -673,19 +673,27 @@ def test_cascade_step(G, Hkv, bs, dtype, part, pfx):
 @pytest.mark.parametrize("name,over,part", [
     ("llama13b", dict(S=6, pool_tokens=16384), 0),
     ("llama13b", dict(S=6, pool_tokens=16384), 256),
+    ("llama13b", dict(S=6, bs=64, pool_tokens=16384, lengths=("fixed", [1, 63, 64, 65, 700, 2048])), 128),
     ("long_gqa", dict(S=3, NB=1024, lengths=("uniform", 700, 4000)), 512),
     ("long_gqa", dict(S=4, NB=1024, lengths=("fixed", [1, 31, 32, 1025])), 0),
+    ("long_gqa", dict(S=3, NB=2048, bs=8, dtype="f16", lengths=("uniform", 1, 3000)), 64),
 ])
-def test_cascade_without_sharing_is_the_fused_step(name, over, part):
-    # with no shared blocks the plan is a plain split-context decode: same
-    # kernels, same partitions, so the same bits as pa_decode_step
+def test_cascade_without_sharing(name, over, part):
+    # no shared blocks: every item is one sequence's partition; the cache
+    # write is exact, the output within the oracle bound, and with G = 8 (the
+    # plain step on the same matrix-core arithmetic) bit-identical to it
     w = synth.make_decode(name, device=DEV, **over)
     note(f"case cascade no-sharing {name} {over} part={part}")
     out1, kc1, vc1 = run_fused(w, part)
     out2, kc2, vc2, plan = run_cascade(w, w.context_lens, part, 0, fused=True)
-    assert plan.n_items == 0
-    assert torch.equal(bits(out1), bits(out2))
+    assert not (plan.items[:, 4] > 1).any()
     assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+    ref, _ = oracle_step(w)
+    err = float(np.max(np.abs(widened(out2, w.dtype) - ref)))
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    if w.Hq // w.Hkv == 8 and part % 32 == 0:
+        assert torch.equal(bits(out1), bits(out2))
 
 
 @pytest.mark.parametrize("full", [False, True])
