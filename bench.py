@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b",
-                    choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix"],
+                    choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix",
+                             "system_prompt"],
                     help="decode workload to time (default: the 13B-shaped batch)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
@@ -63,7 +64,8 @@ def parse():
                     help="shared_prefix: prompt tokens (504 leaves the last shared block "
                          "half full, so forks copy it; 512 fills it)")
     ap.add_argument("--prefix-tokens", type=int, default=0,
-                    help="shared_prefix: tokens per shared-prefix work item (0 = whole prefix)")
+                    help="shared_prefix / system_prompt: tokens per shared-prefix work item "
+                         "(0 = whole prefix)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the plain HBM probe")
@@ -248,30 +250,51 @@ def calibrate_copy(torch):
 
 
 def run_shared_prefix(args, pa, synth, torch):
-    """Parallel sampling: 16 prompts x 4 samples sharing the prompt's blocks.
-    Setup (prefill, fork, per-sample tails with copy-on-write) runs through the
-    library's allocator and kernels; then every sample reserves its next slot
-    and K decode steps are timed twice on the same state: the plain fused
-    step (every sample reads its prompt) and the shared-prefix step
-    (pa_cascade_plan + pa_decode_cascade: each prompt's shared blocks read
-    once per group).  Logical bytes count each sample's whole context."""
+    """Blocks shared between sequences, two workloads:
+      shared_prefix  parallel sampling: 16 prompts x 4 samples forked from
+                     each prompt (copy-on-write on divergence);
+      system_prompt  64 requests whose prompts start with one 1024-token
+                     system prompt, registered once and reused through the
+                     prefix registry.
+    Setup runs through the library's allocator and kernels; then every
+    sequence reserves its next slot and K decode steps are timed twice on the
+    same state: the plain fused step (every sequence reads its whole context)
+    and the shared-prefix step (pa_cascade_plan + pa_decode_cascade: shared
+    blocks read once per group).  Logical bytes count each sequence's whole
+    context."""
     import time
     from paged_kv_cache_198_amd import engine
-    sc = synth.make_shared_prefix(seed=args.seed, device="cuda", prompt_len=args.prompt_len)
-    kv = engine.build_shared_prefix(sc)
+    if args.workload == "system_prompt":
+        sc = synth.make_system_prompt(seed=args.seed, device="cuda")
+        kv = engine.build_system_prompt(sc)
+        desc = (f"system prompt shared across requests: {sc.requests} requests, "
+                f"{sc.system_len}-token system prompt registered once, own prompt uniform "
+                f"[{synth.SYSTEM_PROMPT['own'][0]}, {synth.SYSTEM_PROMPT['own'][1]}] tokens, "
+                f"Hq={sc.Hq}, Hkv={sc.Hkv}, D={sc.D}, {sc.dtype}, block_size {sc.bs}, "
+                f"{sc.NB}-block pool")
+        extra = {"system_len": sc.system_len}
+    else:
+        sc = synth.make_shared_prefix(seed=args.seed, device="cuda", prompt_len=args.prompt_len)
+        kv = engine.build_shared_prefix(sc)
+        desc = (f"shared-prefix parallel sampling: {sc.prompts} prompts x {sc.samples} samples, "
+                f"Hq=Hkv={sc.Hkv}, D={sc.D}, {sc.dtype}, block_size {sc.bs}, prompt "
+                f"{sc.prompt_len} tokens in shared blocks, tails uniform in [0, 256], "
+                f"{sc.NB}-block pool")
+        extra = {"prompt_len": sc.prompt_len}
+    S = sc.q.shape[0]
     fork_copies = kv.copies
-    seqs = list(range(sc.S))
+    seqs = list(range(S))
     _, pairs = kv.reserve(seqs)
     MB = max(-(-kv.alloc.seq_len(s) // sc.bs) for s in seqs)
     tables_h, lens_h32 = kv.alloc.build_batch(seqs, MB)
     tables = torch.from_numpy(tables_h).to("cuda")
     lens = torch.from_numpy(lens_h32).to("cuda")
     mx = int(lens_h32.max())
-    out = torch.empty(sc.S, sc.Hq, sc.D, dtype=sc.q.dtype, device="cuda")
+    out = torch.empty(S, sc.Hq, sc.D, dtype=sc.q.dtype, device="cuda")
     t0 = time.perf_counter()
     plan = pa.pa_cascade_plan(tables_h, lens_h32, sc.bs, sc.Hq, sc.Hkv, 0, args.prefix_tokens)
     plan_us = (time.perf_counter() - t0) * 1e6
-    ws = pa.make_cascade_workspace(sc.S, sc.Hq, sc.D, plan)
+    ws = pa.make_cascade_workspace(S, sc.Hq, sc.D, plan)
 
     def plain():
         pa.pa_decode_step(out, sc.q, sc.step_k, sc.step_v, kv.key_cache, kv.value_cache,
@@ -307,6 +330,37 @@ def run_shared_prefix(args, pa, synth, torch):
     block_bytes = sc.bs * sc.Hkv * sc.D * eb
     unique = unique_blocks * 2 * block_bytes
     private_blocks = kv.logical_blocks(seqs)
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode-attention KV GB/s (logical: each sequence's whole context) + us/step, "
+                  f"{args.workload.replace('_', '-')} batch",
+        "value": gbs(logical, step_ms), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "us_per_step": step_ms * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": sc.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, uniform lengths)",
+        "config": {"workload": desc, "S": S, "seed": args.seed,
+                   "prefix_tokens": args.prefix_tokens, **extra,
+                   "logical_kv_bytes": logical, "cascade_kv_bytes": cascade_bytes,
+                   "unique_kv_bytes": unique},
+        "roofline": {"bound": "hbm", "achieved": gbs(cascade_bytes, step_ms),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs(cascade_bytes, step_ms) / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "whole cascade step (work-item kernel + partition reduce)",
+                     "note": "achieved counts the bytes the cascade must read: each shared "
+                             "prefix once per group, every suffix once"},
+        "plain_fused_step": {"us": plain_ms * 1e3, "logical_GBs": gbs(logical, plain_ms),
+                             "speedup_of_cascade": plain_ms / step_ms},
+        "plan": {"items": plan.n_items, "slots_max": plan.slots_max,
+                 "prefix_rows": plan.prefix_rows, "saved_rows": plan.saved_rows,
+                 "host_plan_us": plan_us},
+        "sharing": {"blocks_used": unique_blocks, "blocks_if_private": private_blocks,
+                    "memory_saving": 1.0 - unique_blocks / private_blocks,
+                    "cow_copies_at_fork": fork_copies, "cow_pairs_this_step": len(pairs)},
+        "cpu_baseline": None,
+    }
+    if args.workload == "system_prompt":
+        return res
 
     # copy-on-write block copies across the layers of a 40-layer model: the
     # fork-time divergence of this batch (one pair per sample that writes
@@ -328,41 +382,9 @@ def run_shared_prefix(args, pa, synth, torch):
     torch.cuda.synchronize()
     cow_ms = start.elapsed_time(stop) / 20
     cow_bytes = 2 * n_pairs * L * 2 * block_bytes          # read + write, K and V
-    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
-    return {
-        "metric": "decode-attention KV GB/s (logical: each sample's whole context) + us/step, "
-                  "shared-prefix batch",
-        "value": gbs(logical, step_ms), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
-        "us_per_step": step_ms * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": sc.dtype,
-        "data": "synthetic (seeded N(0,1) q/K/V, uniform tails)",
-        "config": {"workload": f"shared-prefix parallel sampling: {sc.prompts} prompts x "
-                               f"{sc.samples} samples, Hq=Hkv={sc.Hkv}, D={sc.D}, {sc.dtype}, "
-                               f"block_size {sc.bs}, prompt {sc.prompt_len} tokens in shared "
-                               f"blocks, tails uniform in [0, 256], {sc.NB}-block pool",
-                   "S": sc.S, "prompt_len": sc.prompt_len, "seed": args.seed,
-                   "prefix_tokens": args.prefix_tokens,
-                   "logical_kv_bytes": logical, "cascade_kv_bytes": cascade_bytes,
-                   "unique_kv_bytes": unique},
-        "roofline": {"bound": "hbm", "achieved": gbs(cascade_bytes, step_ms),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs(cascade_bytes, step_ms) / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "whole cascade step (work-item kernel + partition reduce)",
-                     "note": "achieved counts the bytes the cascade must read: each shared "
-                             "prefix once per group, every suffix once"},
-        "plain_fused_step": {"us": plain_ms * 1e3, "logical_GBs": gbs(logical, plain_ms),
-                             "speedup_of_cascade": plain_ms / step_ms},
-        "plan": {"items": plan.n_items, "slots_max": plan.slots_max,
-                 "prefix_rows": plan.prefix_rows, "saved_rows": plan.saved_rows,
-                 "host_plan_us": plan_us},
-        "sharing": {"blocks_used": unique_blocks, "blocks_if_private": private_blocks,
-                    "memory_saving": 1.0 - unique_blocks / private_blocks,
-                    "cow_copies_at_fork": fork_copies, "cow_pairs_this_step": len(pairs)},
-        "cow_copy": {"pairs": n_pairs, "layers": L, "us": cow_ms * 1e3,
-                     "GBs": cow_bytes / (cow_ms * 1e-3) / 1e9},
-        "cpu_baseline": None,
-    }
+    res["cow_copy"] = {"pairs": n_pairs, "layers": L, "us": cow_ms * 1e3,
+                       "GBs": cow_bytes / (cow_ms * 1e-3) / 1e9}
+    return res
 
 
 def main():
@@ -379,8 +401,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     pa.lib()
-    if args.workload == "shared_prefix":
-        print("[bench] building shared-prefix state", file=sys.stderr, flush=True)
+    if args.workload in ("shared_prefix", "system_prompt"):
+        print(f"[bench] building {args.workload} state", file=sys.stderr, flush=True)
         print(json.dumps(run_shared_prefix(args, pa, synth, torch)), flush=True)
         return
     print(f"[bench] building workload {args.workload} bs={args.bs}", file=sys.stderr, flush=True)

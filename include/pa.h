@@ -313,6 +313,36 @@ int pa_seq_blocks(const pa_allocator* a, int64_t seq_id, int32_t* blocks, int32_
 int pa_build_batch(const pa_allocator* a, const int64_t* seq_ids, int32_t S, int32_t MB,
                    int32_t* block_tables, int32_t* context_lens);
 
+/* Prefix registry: sharing across requests ("From the abstract": the cache
+ * is shared within and across requests; "What is left": shared blocks for
+ * common system prompts across users).  The registry maps 64-bit keys to
+ * full blocks and holds one reference to each, so a registered block
+ * outlives the sequence that filled it.  Keys come from the caller, one per
+ * block, and must name the whole prefix up to and including that block
+ * (e.g. a hash chained over the token ids, block by block); the allocator
+ * never sees tokens.  A full block is never written again, so a registered
+ * block stays read-only. */
+
+/* Enters the first n blocks of seq_id (all full: n*bs <= its length) under
+ * keys[0..n).  A key already present keeps its block (first publisher wins);
+ * every new entry adds one reference.  *added = new entries. */
+int pa_prefix_publish(pa_allocator* a, int64_t seq_id, const uint64_t* keys, int32_t n,
+                      int32_t* added);
+/* Creates seq_id starting with the registered blocks of the longest run
+ * keys[0..m) that are all present (m <= n; the run ends at the first
+ * miss), one reference added to each; its length is m*bs tokens and
+ * *matched = m.  The caller appends the rest of the prompt as usual; since
+ * the matched blocks are full, no append copies them. */
+int pa_seq_create_prefixed(pa_allocator* a, int64_t seq_id, const uint64_t* keys, int32_t n,
+                           int32_t* matched);
+/* Removes keys[0..n) from the registry, walking from the last key to the
+ * first: each present entry drops its reference, and a block that reaches
+ * zero goes onto the free stack.  Missing keys are skipped.
+ * *removed = entries removed. */
+int pa_prefix_evict(pa_allocator* a, const uint64_t* keys, int32_t n, int32_t* removed);
+/* Registered entries, -1 for a NULL allocator. */
+int32_t pa_prefix_size(const pa_allocator* a);
+
 /* Snapshot: refcounts[NB]; free_stack[n] in hand-out order (first = next). */
 int pa_alloc_export(const pa_allocator* a, int32_t* refcounts, int32_t* free_stack,
                     int32_t* n_free);

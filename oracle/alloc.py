@@ -23,6 +23,21 @@ Readings where the pages are silent:
   * ``free`` walks the table from the last logical block to the first,
     dropping one reference each and pushing every block that reaches zero;
   * running out of blocks reports ``OOM`` and changes nothing.
+
+Sharing across requests (page "Efficient Memory Management for Large
+Language Model Serving with PagedAttention", from the abstract: sharing
+within and across requests; "PagedAttention: the KV cache was the
+bottleneck all along", section "What is left": shared blocks for common
+system prompts across users).  Readings:
+  * a registry maps caller keys (one per block, naming the whole prefix up
+    to that block) to full blocks and holds one reference to each;
+  * ``publish`` enters a sequence's first n full blocks; a key already
+    present keeps its block;
+  * ``create_prefixed`` starts a sequence with the blocks of the longest run
+    of present keys, stopping at the first miss, one reference each; its
+    length is that many full blocks;
+  * ``evict`` walks its keys from last to first, dropping each present
+    entry's reference and pushing blocks that reach zero.
 """
 from __future__ import annotations
 
@@ -44,6 +59,7 @@ class Allocator:
         self.ref = [0] * num_blocks
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.registry: dict[int, int] = {}    # key -> block
 
     # -- queries -----------------------------------------------------------
     def num_free(self) -> int:
@@ -125,3 +141,44 @@ class Allocator:
             tables.append(t + [-1] * (MB - len(t)))
             lens.append(self.lens[sid])
         return tables, lens
+
+    # -- sharing across requests ------------------------------------------
+    def publish(self, sid: int, keys) -> int:
+        keys = [int(k) for k in keys]
+        if len(keys) * self.bs > self.lens[sid]:
+            raise ValueError("only full blocks can be published")
+        added = 0
+        for j, k in enumerate(keys):
+            if k in self.registry:
+                continue
+            b = self.tables[sid][j]
+            self.registry[k] = b
+            self.ref[b] += 1
+            added += 1
+        return added
+
+    def create_prefixed(self, sid: int, keys) -> int:
+        if sid in self.tables:
+            raise KeyError(f"sequence {sid} exists")
+        blocks = []
+        for k in keys:
+            if int(k) not in self.registry:
+                break
+            blocks.append(self.registry[int(k)])
+        for b in blocks:
+            self.ref[b] += 1
+        self.tables[sid] = blocks
+        self.lens[sid] = len(blocks) * self.bs
+        return len(blocks)
+
+    def evict(self, keys) -> int:
+        removed = 0
+        for k in reversed([int(k) for k in keys]):
+            if k not in self.registry:
+                continue
+            b = self.registry.pop(k)
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+            removed += 1
+        return removed

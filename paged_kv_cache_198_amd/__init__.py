@@ -36,6 +36,7 @@ _lib = None
 _c_int, _c_i32, _c_i64, _c_p = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _p_i32 = ctypes.POINTER(ctypes.c_int32)
 _p_i64 = ctypes.POINTER(ctypes.c_int64)
+_p_u64 = ctypes.POINTER(ctypes.c_uint64)
 
 _SIGNATURES = {
     "pa_version": (_c_int, []),
@@ -74,6 +75,10 @@ _SIGNATURES = {
     "pa_seq_blocks": (_c_int, [_c_p, _c_i64, _p_i32, _c_i32]),
     "pa_build_batch": (_c_int, [_c_p, _p_i64, _c_i32, _c_i32, _p_i32, _p_i32]),
     "pa_alloc_export": (_c_int, [_c_p, _p_i32, _p_i32, _p_i32]),
+    "pa_prefix_publish": (_c_int, [_c_p, _c_i64, _p_u64, _c_i32, _p_i32]),
+    "pa_seq_create_prefixed": (_c_int, [_c_p, _c_i64, _p_u64, _c_i32, _p_i32]),
+    "pa_prefix_evict": (_c_int, [_c_p, _p_u64, _c_i32, _p_i32]),
+    "pa_prefix_size": (_c_i32, [_c_p]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -397,7 +402,8 @@ def pa_copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[to
 # host allocator
 # ---------------------------------------------------------------------------
 class Allocator:
-    """Host block allocator (C++): free list, refcounts, copy-on-write fork."""
+    """Host block allocator (C++): free list, refcounts, copy-on-write fork,
+    prefix registry for sharing across requests."""
 
     def __init__(self, num_blocks: int, bs: int, init_order=None):
         L = lib()
@@ -471,6 +477,39 @@ class Allocator:
                                     tables.ctypes.data_as(_p_i32), lens.ctypes.data_as(_p_i32)),
                "pa_build_batch")
         return tables, lens
+
+    # -- prefix registry (sharing across requests) --------------------------
+    @staticmethod
+    def _keys(keys) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(keys, dtype=np.uint64).reshape(-1))
+
+    def prefix_publish(self, seq_id: int, keys) -> int:
+        """Register the sequence's first len(keys) full blocks; returns the
+        number of new entries."""
+        k = self._keys(keys)
+        added = ctypes.c_int32()
+        _check(lib().pa_prefix_publish(self._h, seq_id, k.ctypes.data_as(_p_u64), k.size,
+                                       ctypes.byref(added)), "pa_prefix_publish")
+        return added.value
+
+    def create_prefixed(self, seq_id: int, keys) -> int:
+        """New sequence starting with the registered blocks of the longest
+        run of present keys; returns that run's length in blocks."""
+        k = self._keys(keys)
+        matched = ctypes.c_int32()
+        _check(lib().pa_seq_create_prefixed(self._h, seq_id, k.ctypes.data_as(_p_u64), k.size,
+                                            ctypes.byref(matched)), "pa_seq_create_prefixed")
+        return matched.value
+
+    def prefix_evict(self, keys) -> int:
+        k = self._keys(keys)
+        removed = ctypes.c_int32()
+        _check(lib().pa_prefix_evict(self._h, k.ctypes.data_as(_p_u64), k.size,
+                                     ctypes.byref(removed)), "pa_prefix_evict")
+        return removed.value
+
+    def prefix_size(self) -> int:
+        return lib().pa_prefix_size(self._h)
 
     def export(self):
         """(refcounts [NB], free blocks in hand-out order)."""

@@ -7,6 +7,12 @@
 // tie-break rules (LIFO free stack, lazy copy-on-write, release order, OOM
 // leaving the state unchanged) are stated in include/pa.h.
 //
+// Sharing across requests ("From the abstract": sharing within and across
+// requests; "What is left": common system prompts shared across users): a
+// prefix registry maps caller keys to full blocks and holds one reference
+// to each, so a later request whose prompt starts the same way takes those
+// blocks instead of writing its own.
+//
 // Plain C++17 with no HIP dependency: it runs on the scheduler's host thread.
 #include <algorithm>
 #include <cstdint>
@@ -31,6 +37,7 @@ struct pa_allocator {
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<uint64_t, int32_t> prefix;  // key -> full block (one reference each)
 
   int32_t pop() {
     int32_t b = free_stack.back();
@@ -189,6 +196,61 @@ int pa_build_batch(const pa_allocator* a, const int64_t* seq_ids, int32_t S, int
     context_lens[i] = static_cast<int32_t>(s->len);
   }
   return PA_OK;
+}
+
+int pa_prefix_publish(pa_allocator* a, int64_t seq_id, const uint64_t* keys, int32_t n,
+                      int32_t* added) {
+  if (added) *added = 0;
+  if (!a || n < 0 || (n > 0 && !keys)) return PA_ERR_INVALID;
+  const Seq* s = a->find(seq_id);
+  if (!s || static_cast<int64_t>(n) * a->bs > s->len) return PA_ERR_INVALID;
+  int32_t count = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    // a key that is already present keeps its block (first publisher wins)
+    if (a->prefix.emplace(keys[j], s->blocks[j]).second) {
+      a->ref[s->blocks[j]] += 1;
+      ++count;
+    }
+  }
+  if (added) *added = count;
+  return PA_OK;
+}
+
+int pa_seq_create_prefixed(pa_allocator* a, int64_t seq_id, const uint64_t* keys, int32_t n,
+                           int32_t* matched) {
+  if (matched) *matched = 0;
+  if (!a || n < 0 || (n > 0 && !keys) || a->find(seq_id)) return PA_ERR_INVALID;
+  Seq s;
+  for (int32_t j = 0; j < n; ++j) {
+    auto it = a->prefix.find(keys[j]);
+    if (it == a->prefix.end()) break;      // the run of hits ends at the first miss
+    s.blocks.push_back(it->second);
+  }
+  for (int32_t b : s.blocks) a->ref[b] += 1;
+  s.len = static_cast<int64_t>(s.blocks.size()) * a->bs;
+  if (matched) *matched = static_cast<int32_t>(s.blocks.size());
+  a->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+int pa_prefix_evict(pa_allocator* a, const uint64_t* keys, int32_t n, int32_t* removed) {
+  if (removed) *removed = 0;
+  if (!a || n < 0 || (n > 0 && !keys)) return PA_ERR_INVALID;
+  int32_t count = 0;
+  for (int32_t j = n - 1; j >= 0; --j) {  // last to first, as a table is released
+    auto it = a->prefix.find(keys[j]);
+    if (it == a->prefix.end()) continue;
+    const int32_t b = it->second;
+    a->prefix.erase(it);
+    if (--a->ref[b] == 0) a->free_stack.push_back(b);
+    ++count;
+  }
+  if (removed) *removed = count;
+  return PA_OK;
+}
+
+int32_t pa_prefix_size(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->prefix.size()) : -1;
 }
 
 int pa_alloc_export(const pa_allocator* a, int32_t* refcounts, int32_t* free_stack,

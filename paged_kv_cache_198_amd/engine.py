@@ -45,6 +45,27 @@ class PagedKV:
                                 torch.from_numpy(slots).to(self.device))
         return slots
 
+    def publish(self, seq_id: int, keys) -> int:
+        """Register the sequence's first len(keys) full blocks for reuse by
+        later requests (keys name the prefix up to each block)."""
+        return self.alloc.prefix_publish(seq_id, keys)
+
+    def prefill_prefixed(self, seq_id: int, keys, key: torch.Tensor,
+                         value: torch.Tensor) -> int:
+        """New request whose prompt ([T, Hkv, D]) may start with registered
+        blocks: those are taken from the registry and only the rest of the
+        prompt is stored.  Returns the number of prompt tokens reused."""
+        m = self.alloc.create_prefixed(seq_id, keys) * self.bs
+        if key.shape[0] > m:
+            slots, src, dst = self.alloc.append_n(seq_id, key.shape[0] - m)
+            assert src < 0                    # the reused blocks are full
+            pa.pa_reshape_and_cache(key[m:], value[m:], self.key_cache, self.value_cache,
+                                    torch.from_numpy(slots).to(self.device))
+        return m
+
+    def evict(self, keys) -> int:
+        return self.alloc.prefix_evict(keys)
+
     def fork(self, parent: int, child: int) -> None:
         self.alloc.fork(parent, child)
 
@@ -152,4 +173,22 @@ def build_shared_prefix(sc, device="cuda") -> PagedKV:
         sel = torch.tensor(who, device=device)
         kv.append(who, sc.tail_k[:, t].index_select(0, sel).contiguous(),
                   sc.tail_v[:, t].index_select(0, sel).contiguous())
+    return kv
+
+
+def build_system_prompt(sc, device="cuda") -> PagedKV:
+    """The state of a ``synth.SystemPromptScript``: request 0 stores its
+    whole prompt and publishes the system prompt's full blocks; every later
+    request takes those blocks from the registry and stores only its own
+    tokens.  The decode step's token is not yet appended."""
+    kv = PagedKV(sc.NB, sc.bs, sc.Hkv, sc.D, sc.dtype, init_order=sc.init_order, device=device,
+                 key_cache=sc.key_cache.clone(), value_cache=sc.value_cache.clone())
+    keys = sc.system_keys()
+    for r in range(sc.requests):
+        k, v = sc.prompt(r)
+        if r == 0:
+            kv.prefill(0, k, v)
+            kv.publish(0, keys)
+        else:
+            kv.prefill_prefixed(r, keys, k, v)
     return kv

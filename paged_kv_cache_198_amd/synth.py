@@ -315,6 +315,76 @@ def make_forked(seed: int = 0, device="cpu", **over) -> DecodeWorkload:
         key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
 
 
+# Requests that share a system prompt (page "PagedAttention: the KV cache was
+# the bottleneck all along", section "What is left": common system prompts
+# across users; page "Efficient Memory Management for Large Language Model
+# Serving with PagedAttention", from the abstract: sharing across requests).
+# Every request's prompt is the same system prompt followed by its own text.
+SYSTEM_PROMPT = dict(requests=64, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16, NB=8192,
+                     system_len=1024, own=(16, 512))
+
+
+@dataclasses.dataclass
+class SystemPromptScript:
+    seed: int
+    requests: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    dtype: str
+    scale: float
+    system_len: int
+    own_lens: np.ndarray          # int32 [R] tokens after the system prompt
+    init_order: np.ndarray        # int32 [NB]
+    system_k: torch.Tensor        # [system_len, Hkv, D]
+    system_v: torch.Tensor
+    own_k: torch.Tensor           # [R, max_own, Hkv, D]
+    own_v: torch.Tensor
+    step_k: torch.Tensor          # [R, Hkv, D] the decode step's token
+    step_v: torch.Tensor
+    q: torch.Tensor               # [R, Hq, D]
+    key_cache: torch.Tensor       # [NB, Hkv, bs, D] initial pool, all NaN
+    value_cache: torch.Tensor
+
+    def system_keys(self) -> list:
+        """One registry key per full block of the system prompt (standing in
+        for a hash chained over its token ids)."""
+        return [(1 << 40) + j for j in range(self.system_len // self.bs)]
+
+    def prompt(self, r: int):
+        """Request r's whole prompt, K and V [system_len + own, Hkv, D]."""
+        n = int(self.own_lens[r])
+        return (torch.cat([self.system_k, self.own_k[r, :n]]),
+                torch.cat([self.system_v, self.own_v[r, :n]]))
+
+
+def make_system_prompt(seed: int = 0, device="cpu", **over) -> SystemPromptScript:
+    cfg = dict(SYSTEM_PROMPT)
+    cfg.update(over)
+    rng = np.random.default_rng(seed)
+    R, bs, NB = cfg["requests"], cfg["bs"], cfg["NB"]
+    own = rng.integers(cfg["own"][0], cfg["own"][1] + 1, size=R).astype(np.int32)
+    init_order = rng.permutation(NB).astype(np.int32)
+    gen = _generator(seed, device)
+    dt, Hkv, Hq, D, L = cfg["dtype"], cfg["Hkv"], cfg["Hq"], cfg["D"], cfg["system_len"]
+    mo = int(own.max()) if R else 0
+    sk = _randn((L, Hkv, D), gen, device, dt)
+    sv = _randn((L, Hkv, D), gen, device, dt)
+    ok = _randn((R, mo, Hkv, D), gen, device, dt)
+    ov = _randn((R, mo, Hkv, D), gen, device, dt)
+    tk = _randn((R, Hkv, D), gen, device, dt)
+    tv = _randn((R, Hkv, D), gen, device, dt)
+    q = _randn((R, Hq, D), gen, device, dt)
+    kc = torch.full((NB, Hkv, bs, D), float("nan"), device=device, dtype=KV_DTYPES[dt])
+    return SystemPromptScript(
+        seed=seed, requests=R, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
+        scale=float(np.float32(1.0 / np.sqrt(D))), system_len=L, own_lens=own,
+        init_order=init_order, system_k=sk, system_v=sv, own_k=ok, own_v=ov, step_k=tk,
+        step_v=tv, q=q, key_cache=kc, value_cache=kc.clone())
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     """Host copy of a KV-dtype tensor as its raw storage: float32 / float16 as
     themselves, bfloat16 as its uint16 bit patterns (numpy has no bfloat16)."""

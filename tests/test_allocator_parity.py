@@ -114,6 +114,101 @@ def test_random_ops_match_oracle(seed):
     assert tables.tolist() == ot and lens.tolist() == ol
 
 
+def test_prefix_golden_trace():
+    with open(os.path.join(GOLDEN, "prefix_registry_trace.json")) as f:
+        doc = json.load(f)
+    a = pa.Allocator(doc["num_blocks"], doc["bs"])
+    for op in doc["ops"]:
+        kind, why = op["op"], op.get("why", op["op"])
+        if kind == "create":
+            a.create(op["seq"])
+        elif kind == "append_n":
+            slots, src, dst = a.append_n(op["seq"], op["n"])
+            assert slots.tolist() == op["expect_slots"] and (src, dst) == (-1, -1), why
+        elif kind == "append":
+            assert list(a.append(op["seq"])) == op["expect"], why
+        elif kind == "publish":
+            assert a.prefix_publish(op["seq"], op["keys"]) == op["expect"], why
+        elif kind == "create_prefixed":
+            assert a.create_prefixed(op["seq"], op["keys"]) == op["expect"], why
+            assert a.seq_blocks(op["seq"]) == op["table"] and a.seq_len(op["seq"]) == op["len"]
+        elif kind == "evict":
+            assert a.prefix_evict(op["keys"]) == op["expect"], why
+        elif kind == "release":
+            a.free(op["seq"])
+        ref, free = a.export()
+        assert ref == op["ref_after"] and free == op["free_after"], why
+    assert a.prefix_size() == doc["final_registry_size"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_random_ops_match_oracle(seed):
+    """Requests reusing chained prompt keys, with forks, appends, releases
+    and evictions, on both allocators."""
+    rng = np.random.default_rng(100 + seed)
+    NB, bs = 48, int(rng.choice([2, 4, 16]))
+    order = rng.permutation(NB)
+    a = pa.Allocator(NB, bs, init_order=order)
+    o = OracleAllocator(NB, bs, init_order=order)
+    prompts = [[(1 << 40) + 1000 * p + j for j in range(int(rng.integers(1, 7)))]
+               for p in range(4)]
+    live, nxt = [], 0
+    for step in range(2000):
+        r = rng.random()
+        if r < 0.12 or not live:
+            keys = prompts[rng.integers(4)]
+            keys = keys[:int(rng.integers(0, len(keys) + 1))]
+            assert a.create_prefixed(nxt, keys) == o.create_prefixed(nxt, keys)
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.6:
+            sid = live[rng.integers(len(live))]
+            try:
+                expect = o.append(sid)
+            except OracleOOM:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append(sid)
+            else:
+                assert a.append(sid) == expect
+        elif r < 0.7:
+            sid = live[rng.integers(len(live))]
+            keys = prompts[rng.integers(4)]
+            keys = keys[:min(len(keys), o.seq_len(sid) // bs)]
+            assert a.prefix_publish(sid, keys) == o.publish(sid, keys)
+        elif r < 0.78:
+            p = live[rng.integers(len(live))]
+            a.fork(p, nxt)
+            o.fork(p, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.9:
+            sid = live.pop(rng.integers(len(live)))
+            a.free(sid)
+            o.release(sid)
+        else:
+            keys = prompts[rng.integers(4)]
+            assert a.prefix_evict(keys) == o.evict(keys)
+        assert a.prefix_size() == len(o.registry)
+        if step % 25 == 0:
+            state(a, o, live)
+    state(a, o, live)
+
+
+def test_prefix_bad_arguments():
+    a = pa.Allocator(8, 4)
+    a.create(1)
+    a.append_n(1, 6)
+    with pytest.raises(pa.PaError):
+        a.prefix_publish(1, [10, 11])          # block 1 is not full
+    with pytest.raises(pa.PaError):
+        a.prefix_publish(99, [10])             # unknown sequence
+    with pytest.raises(pa.PaError):
+        a.create_prefixed(1, [10])             # id in use
+    assert a.prefix_publish(1, [10]) == 1
+    assert a.create_prefixed(2, []) == 0 and a.seq_len(2) == 0
+    assert a.prefix_evict([]) == 0 and a.prefix_size() == 1
+
+
 def rebuild(o, snap, sid):
     """The oracle applies appends one at a time; undo a partial run that hit
     out-of-blocks so both sides stay in the all-or-nothing state."""

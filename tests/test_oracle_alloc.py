@@ -24,11 +24,14 @@ def snapshot(a):
 
 
 def check_invariants(a):
-    # every reference is one table entry; free + referenced = pool
+    # every reference is one table entry or one registry entry; free +
+    # referenced = pool
     counts = [0] * a.NB
     for t in a.tables.values():
         for b in t:
             counts[b] += 1
+    for b in getattr(a, "registry", {}).values():
+        counts[b] += 1
     assert counts == a.ref
     assert len(a.free) + sum(1 for r in a.ref if r > 0) == a.NB
     assert all(a.ref[b] == 0 for b in a.free)
@@ -161,7 +164,115 @@ def pin_sharing_saving():
     assert abs((1 - used / private) - (1 - 38 / 134)) < 1e-15
 
 
-PINS = [pin_trace, pin_random_ops, pin_tail_only_waste, pin_lazy_cow_count, pin_sharing_saving]
+def pin_prefix_trace():
+    with open(os.path.join(GOLDEN, "prefix_registry_trace.json")) as f:
+        doc = json.load(f)
+    a = Allocator(doc["num_blocks"], doc["bs"])
+    for op in doc["ops"]:
+        kind, why = op["op"], op.get("why", op["op"])
+        if kind == "create":
+            a.create(op["seq"])
+        elif kind == "append_n":
+            assert [a.append(op["seq"])[0] for _ in range(op["n"])] == op["expect_slots"], why
+        elif kind == "append":
+            assert list(a.append(op["seq"])) == op["expect"], why
+        elif kind == "publish":
+            assert a.publish(op["seq"], op["keys"]) == op["expect"], why
+        elif kind == "create_prefixed":
+            assert a.create_prefixed(op["seq"], op["keys"]) == op["expect"], why
+            assert a.table(op["seq"]) == op["table"] and a.seq_len(op["seq"]) == op["len"], why
+        elif kind == "evict":
+            assert a.evict(op["keys"]) == op["expect"], why
+        elif kind == "release":
+            a.release(op["seq"])
+        assert a.ref == op["ref_after"], why
+        assert a.free_stack() == op["free_after"], why
+        check_invariants(a)
+    assert len(a.registry) == doc["final_registry_size"] and not a.tables
+
+
+def pin_prefix_random_ops(seed=1, steps=3000):
+    """Random requests that publish and reuse chained prefixes, forks,
+    appends, releases and evictions, with the invariants after every step:
+    references = table entries + registry entries, registered blocks are never
+    free, a prefixed sequence starts with registered blocks, and appending
+    after a full match never copies."""
+    rng = np.random.default_rng(seed)
+    a = Allocator(48, 4, init_order=rng.permutation(48))
+    # chained keys of four "system prompts" of 1..6 blocks
+    prompts = [[1000 * p + j for j in range(int(rng.integers(1, 7)))] for p in range(4)]
+    live, nxt = [], 0
+    for _ in range(steps):
+        r = rng.random()
+        try:
+            if r < 0.12 or not live:
+                keys = prompts[rng.integers(4)]
+                n = int(rng.integers(0, len(keys) + 1))
+                m = a.create_prefixed(nxt, keys[:n])
+                assert a.table(nxt) == [a.registry[k] for k in keys[:m]]
+                assert m == n or keys[m] not in a.registry
+                assert a.seq_len(nxt) == m * a.bs
+                live.append(nxt)
+                nxt += 1
+                if m:
+                    slot, src, dst = a.append(nxt - 1)       # full blocks: no copy
+                    assert (src, dst) == (-1, -1)
+            elif r < 0.6:
+                sid = live[rng.integers(len(live))]
+                a.append(sid)
+            elif r < 0.7:
+                sid = live[rng.integers(len(live))]
+                keys = prompts[rng.integers(4)]
+                n = min(len(keys), a.seq_len(sid) // a.bs)
+                before = dict(a.registry)
+                added = a.publish(sid, keys[:n])
+                assert added == sum(1 for k in keys[:n] if k not in before)
+                assert all(a.registry[k] == before[k] for k in before)
+            elif r < 0.78:
+                p = live[rng.integers(len(live))]
+                a.fork(p, nxt)
+                live.append(nxt)
+                nxt += 1
+            elif r < 0.88:
+                a.release(live.pop(rng.integers(len(live))))
+            else:
+                keys = prompts[rng.integers(4)]
+                present = sum(1 for k in keys if k in a.registry)
+                assert a.evict(keys) == present
+        except OutOfBlocks:
+            pass
+        check_invariants(a)
+        assert not set(a.registry.values()) & set(a.free)
+    for sid in list(live):
+        a.release(sid)
+    for keys in prompts:
+        a.evict(keys)
+    assert a.num_free() == a.NB and all(r == 0 for r in a.ref) and not a.registry
+
+
+def pin_system_prompt_saving():
+    """N requests that share a 64-block system prompt through the registry
+    hold 64 + their own blocks; private prompts would hold N * 64 more."""
+    a = Allocator(1024, 16)
+    keys = list(range(64))
+    a.create(0)
+    for _ in range(64 * 16):
+        a.append(0)
+    assert a.publish(0, keys) == 64
+    own = [0, 1, 15, 16, 17, 100]
+    for r, n in enumerate(own, start=1):
+        assert a.create_prefixed(r, keys) == 64
+        for _ in range(n):
+            assert a.append(r)[1:] == (-1, -1)
+    used = a.NB - a.num_free()
+    mine = sum(-(-n // 16) for n in own)
+    assert used == 64 + mine
+    private = (len(own) + 1) * 64 + mine
+    assert private - used == len(own) * 64
+
+
+PINS = [pin_trace, pin_random_ops, pin_tail_only_waste, pin_lazy_cow_count, pin_sharing_saving,
+        pin_prefix_trace, pin_prefix_random_ops, pin_system_prompt_saving]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

@@ -209,9 +209,76 @@ class LeakyReleaseAllocator(oa.Allocator):
                 self.free.append(b)
 
 
+class PublishNoRefAllocator(oa.Allocator):
+    """The registry does not hold a reference to its blocks."""
+    def publish(self, sid, keys):
+        added = 0
+        for j, k in enumerate(int(k) for k in keys):
+            if k not in self.registry:
+                self.registry[k] = self.tables[sid][j]
+                added += 1
+        return added
+
+
+class PublishOverwriteAllocator(oa.Allocator):
+    """A repeated key takes the newer block (last publisher wins)."""
+    def publish(self, sid, keys):
+        added = 0
+        for j, k in enumerate(int(k) for k in keys):
+            b = self.tables[sid][j]
+            if k in self.registry:
+                old = self.registry[k]
+                if old == b:
+                    continue
+                self.ref[old] -= 1
+                if self.ref[old] == 0:
+                    self.free.append(old)
+            else:
+                added += 1
+            self.registry[k] = b
+            self.ref[b] += 1
+        return added
+
+
+class PrefixSkipsMissAllocator(oa.Allocator):
+    """Takes every present key instead of stopping at the first miss."""
+    def create_prefixed(self, sid, keys):
+        blocks = [self.registry[int(k)] for k in keys if int(k) in self.registry]
+        for b in blocks:
+            self.ref[b] += 1
+        self.tables[sid] = blocks
+        self.lens[sid] = len(blocks) * self.bs
+        return len(blocks)
+
+
+class PrefixZeroLengthAllocator(oa.Allocator):
+    """Shares the blocks but forgets the tokens they hold."""
+    def create_prefixed(self, sid, keys):
+        m = super().create_prefixed(sid, keys)
+        self.lens[sid] = 0
+        return m
+
+
+class ForwardEvictAllocator(oa.Allocator):
+    def evict(self, keys):
+        removed = 0
+        for k in (int(k) for k in keys):
+            if k in self.registry:
+                b = self.registry.pop(k)
+                self.ref[b] -= 1
+                if self.ref[b] == 0:
+                    self.free.append(b)
+                removed += 1
+        return removed
+
+
 ALLOC_MUTANTS = {"fifo": FifoAllocator, "eager_cow": EagerCowAllocator,
                  "forward_release": ForwardReleaseAllocator, "no_cow": NoCowAllocator,
-                 "leaky_release": LeakyReleaseAllocator}
+                 "leaky_release": LeakyReleaseAllocator, "publish_no_ref": PublishNoRefAllocator,
+                 "publish_overwrite": PublishOverwriteAllocator,
+                 "prefix_skips_miss": PrefixSkipsMissAllocator,
+                 "prefix_zero_length": PrefixZeroLengthAllocator,
+                 "forward_evict": ForwardEvictAllocator}
 
 
 @pytest.mark.parametrize("name", sorted(ALLOC_MUTANTS))
