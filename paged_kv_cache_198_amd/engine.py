@@ -22,27 +22,55 @@ _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 class PagedKV:
+    """Paged K/V pools for ``layers`` attention layers that share one block
+    table per sequence (a block index names the same slots in every layer's
+    pool), and the allocator that hands out those blocks.  Per-token inputs
+    are ``[T, Hkv, D]`` for one layer or ``[layers, T, Hkv, D]``."""
+
     def __init__(self, num_blocks: int, bs: int, Hkv: int, D: int, dtype: str,
                  init_order=None, device="cuda", key_cache: Optional[torch.Tensor] = None,
-                 value_cache: Optional[torch.Tensor] = None):
+                 value_cache: Optional[torch.Tensor] = None, layers: int = 1):
         self.NB, self.bs, self.Hkv, self.D, self.dtype = num_blocks, bs, Hkv, D, dtype
         self.device = device
+        self.layers = layers
         shape = (num_blocks, Hkv, bs, D)
-        self.key_cache = key_cache if key_cache is not None else torch.zeros(
-            shape, dtype=_DT[dtype], device=device)
-        self.value_cache = value_cache if value_cache is not None else torch.zeros(
-            shape, dtype=_DT[dtype], device=device)
+        if key_cache is not None:
+            assert layers == 1 and value_cache is not None
+            self.key_caches, self.value_caches = [key_cache], [value_cache]
+        else:
+            self.key_caches = [torch.zeros(shape, dtype=_DT[dtype], device=device)
+                               for _ in range(layers)]
+            self.value_caches = [torch.zeros(shape, dtype=_DT[dtype], device=device)
+                                 for _ in range(layers)]
         self.alloc = pa.Allocator(num_blocks, bs, init_order=init_order)
-        self.copies = 0                       # block copies issued so far
+        self.copies = 0                       # block copies issued so far (per layer)
+
+    @property
+    def key_cache(self) -> torch.Tensor:
+        return self.key_caches[0]
+
+    @property
+    def value_cache(self) -> torch.Tensor:
+        return self.value_caches[0]
+
+    def _per_layer(self, t: torch.Tensor):
+        return [t] if t.dim() == 3 else [t[i] for i in range(t.shape[0])]
+
+    def _store(self, key: torch.Tensor, value: torch.Tensor, slots) -> None:
+        ks, vs = self._per_layer(key), self._per_layer(value)
+        assert len(ks) == self.layers
+        sl = torch.as_tensor(slots, dtype=torch.int64).to(self.device)
+        for kc, vc, k, v in zip(self.key_caches, self.value_caches, ks, vs):
+            pa.pa_reshape_and_cache(k.contiguous(), v.contiguous(), kc, vc, sl)
 
     # -- sequences ---------------------------------------------------------
     def prefill(self, seq_id: int, key: torch.Tensor, value: torch.Tensor) -> np.ndarray:
-        """New sequence holding the prompt's ``T`` tokens ([T, Hkv, D])."""
+        """New sequence holding the prompt's ``T`` tokens."""
         self.alloc.create(seq_id)
-        slots, src, dst = self.alloc.append_n(seq_id, key.shape[0])
+        T = key.shape[-3]
+        slots, src, dst = self.alloc.append_n(seq_id, T)
         assert src < 0                        # a new sequence shares nothing
-        pa.pa_reshape_and_cache(key, value, self.key_cache, self.value_cache,
-                                torch.from_numpy(slots).to(self.device))
+        self._store(key, value, slots)
         return slots
 
     def publish(self, seq_id: int, keys) -> int:
@@ -56,11 +84,14 @@ class PagedKV:
         blocks: those are taken from the registry and only the rest of the
         prompt is stored.  Returns the number of prompt tokens reused."""
         m = self.alloc.create_prefixed(seq_id, keys) * self.bs
-        if key.shape[0] > m:
-            slots, src, dst = self.alloc.append_n(seq_id, key.shape[0] - m)
+        T = key.shape[-3]
+        if T > m:
+            slots, src, dst = self.alloc.append_n(seq_id, T - m)
             assert src < 0                    # the reused blocks are full
-            pa.pa_reshape_and_cache(key[m:], value[m:], self.key_cache, self.value_cache,
-                                    torch.from_numpy(slots).to(self.device))
+            if key.dim() == 3:
+                self._store(key[m:], value[m:], slots)
+            else:
+                self._store(key[:, m:], value[:, m:], slots)
         return m
 
     def evict(self, keys) -> int:
@@ -82,15 +113,16 @@ class PagedKV:
             if src >= 0:
                 pairs.append((src, dst))
         if pairs:
-            pa.pa_copy_blocks([self.key_cache], [self.value_cache], pairs)
+            # one call copies the pairs in every layer's pools
+            pa.pa_copy_blocks(self.key_caches, self.value_caches, pairs)
             self.copies += len(pairs)
         return np.asarray(slots, dtype=np.int64), pairs
 
     def append(self, seq_ids: Sequence[int], key: torch.Tensor, value: torch.Tensor):
-        """Store one token per sequence ([S, Hkv, D]) at its next position."""
+        """Store one token per sequence ([S, Hkv, D] or [layers, S, Hkv, D])
+        at its next position."""
         slots, pairs = self.reserve(seq_ids)
-        pa.pa_reshape_and_cache(key, value, self.key_cache, self.value_cache,
-                                torch.from_numpy(slots).to(self.device))
+        self._store(key, value, slots)
         return slots, pairs
 
     # -- batches -----------------------------------------------------------
@@ -103,13 +135,16 @@ class PagedKV:
                 int(lens.max()) if len(lens) else 0)
 
     def decode(self, query: torch.Tensor, seq_ids: Sequence[int], scale: float,
-               partition_tokens: int = 0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Attention over each sequence's current context (no new token)."""
+               partition_tokens: int = 0, out: Optional[torch.Tensor] = None,
+               layer: int = 0) -> torch.Tensor:
+        """Attention over each sequence's current context (no new token) in
+        one layer."""
         tables, lens, mx = self.batch(seq_ids)
         out = torch.empty_like(query) if out is None else out
         ws = pa.make_workspace(query.shape[0], query.shape[1], self.D, mx, partition_tokens,
                                device=self.device)
-        pa.pa_decode_attention(out, query, self.key_cache, self.value_cache, tables, lens, mx,
+        pa.pa_decode_attention(out, query, self.key_caches[layer], self.value_caches[layer],
+                               tables, lens, mx,
                                scale, partition_tokens, ws)
         return out
 
@@ -117,14 +152,18 @@ class PagedKV:
              value: torch.Tensor, scale: float, partition_tokens: int = 0,
              out: Optional[torch.Tensor] = None) -> torch.Tensor:
         """One decode step: reserve each sequence's next slot (copying shared
-        blocks first), then store the new token and attend in one launch."""
+        blocks in every layer first), then, per layer, store the new token
+        and attend in one launch.  query [S, Hq, D] or [layers, S, Hq, D]."""
         self.reserve(seq_ids)
         tables, lens, mx = self.batch(seq_ids)
+        qs, ks, vs = self._per_layer(query), self._per_layer(key), self._per_layer(value)
         out = torch.empty_like(query) if out is None else out
-        ws = pa.make_workspace(query.shape[0], query.shape[1], self.D, mx, partition_tokens,
+        outs = self._per_layer(out)
+        ws = pa.make_workspace(qs[0].shape[0], qs[0].shape[1], self.D, mx, partition_tokens,
                                device=self.device)
-        pa.pa_decode_step(out, query, key, value, self.key_cache, self.value_cache, tables,
-                          lens, mx, scale, partition_tokens, ws)
+        for i in range(self.layers):
+            pa.pa_decode_step(outs[i], qs[i], ks[i], vs[i], self.key_caches[i],
+                              self.value_caches[i], tables, lens, mx, scale, partition_tokens, ws)
         return out
 
     def step_cascade(self, query: torch.Tensor, seq_ids: Sequence[int], key: torch.Tensor,
@@ -136,16 +175,19 @@ class PagedKV:
         self.reserve(seq_ids)
         MB = max(-(-self.alloc.seq_len(s) // self.bs) for s in seq_ids)
         tables, lens = self.alloc.build_batch(list(seq_ids), max(MB, 1))
-        S, Hq = query.shape[0], query.shape[1]
+        qs, ks, vs = self._per_layer(query), self._per_layer(key), self._per_layer(value)
+        S, Hq = qs[0].shape[0], qs[0].shape[1]
         plan = pa.pa_cascade_plan(tables, lens, self.bs, Hq, self.Hkv, partition_tokens,
                                   prefix_tokens)
         out = torch.empty_like(query) if out is None else out
+        outs = self._per_layer(out)
         ws = pa.make_cascade_workspace(S, Hq, self.D, plan, device=self.device)
-        pa.pa_decode_cascade(out, query, self.key_cache, self.value_cache,
-                             torch.from_numpy(tables).to(self.device),
-                             torch.from_numpy(lens).to(self.device), plan,
-                             int(lens.max()) if len(lens) else 1, scale, partition_tokens, ws,
-                             key=key, value=value)
+        tables_d = torch.from_numpy(tables).to(self.device)
+        lens_d = torch.from_numpy(lens).to(self.device)
+        for i in range(self.layers):     # one plan serves every layer
+            pa.pa_decode_cascade(outs[i], qs[i], self.key_caches[i], self.value_caches[i],
+                                 tables_d, lens_d, plan, int(lens.max()) if len(lens) else 1,
+                                 scale, partition_tokens, ws, key=ks[i], value=vs[i])
         return out, plan
 
     # -- accounting --------------------------------------------------------
@@ -154,6 +196,32 @@ class PagedKV:
 
     def logical_blocks(self, seq_ids: Sequence[int]) -> int:
         return sum(-(-self.alloc.seq_len(s) // self.bs) for s in seq_ids)
+
+
+def beam_reselect(kv: PagedKV, beams, choices, next_id: int):
+    """One beam-search selection ("Virtual memory for attention": beams are
+    forked and discarded).  ``beams[r]`` lists request r's live beam ids;
+    ``choices[r][i]`` is the index, in ``beams[r]``, of the beam that new beam
+    i continues.  A beam chosen once continues under its own id; every
+    further choice forks it under a new id; a beam nobody chose is freed.
+    Forks come first, in choice order, then the frees, in beam order.
+    Returns (new beam lists, next unused id)."""
+    out = []
+    for cur, pick in zip(beams, choices):
+        used, nxt = set(), []
+        for i in pick:
+            if i not in used:
+                used.add(i)
+                nxt.append(cur[i])
+            else:
+                kv.fork(cur[i], next_id)
+                nxt.append(next_id)
+                next_id += 1
+        for i, sid in enumerate(cur):
+            if i not in used:
+                kv.free(sid)
+        out.append(nxt)
+    return out, next_id
 
 
 def build_shared_prefix(sc, device="cuda") -> PagedKV:

@@ -385,6 +385,66 @@ def make_system_prompt(seed: int = 0, device="cpu", **over) -> SystemPromptScrip
         step_v=tv, q=q, key_cache=kc, value_cache=kc.clone())
 
 
+# Beam search (page "PagedAttention: the KV cache was the bottleneck all
+# along", section "Virtual memory for attention": beams share more than
+# parallel samples and are forked and discarded all the time).  There are no
+# model scores, so which beams survive is drawn at random: at every step each
+# of a request's W new beams picks its parent uniformly among the W current
+# ones (with replacement), so some beams fork and others are dropped.
+BEAM = dict(requests=3, width=4, layers=3, Hq=8, Hkv=4, D=128, dtype="bf16", bs=8, NB=1024,
+            prompt=(40, 90), steps=12)
+
+
+@dataclasses.dataclass
+class BeamScript:
+    seed: int
+    requests: int
+    width: int
+    layers: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    dtype: str
+    scale: float
+    steps: int
+    prompt_lens: np.ndarray       # int32 [R]
+    choices: np.ndarray           # int32 [steps, R, W] parent index of each new beam
+    init_order: np.ndarray        # int32 [NB]
+    prompt_k: list                # R tensors [layers, prompt_len, Hkv, D]
+    prompt_v: list
+    step_k: torch.Tensor          # [steps, layers, R*W, Hkv, D] each step's new token
+    step_v: torch.Tensor
+    q: torch.Tensor               # [layers, R*W, Hq, D] queries of the final step
+    key_cache: torch.Tensor       # [NB, Hkv, bs, D] initial pool of every layer, all NaN
+    value_cache: torch.Tensor
+
+
+def make_beam(seed: int = 0, device="cpu", **over) -> BeamScript:
+    cfg = dict(BEAM)
+    cfg.update(over)
+    rng = np.random.default_rng(seed)
+    R, W, L, T = cfg["requests"], cfg["width"], cfg["layers"], cfg["steps"]
+    lens = rng.integers(cfg["prompt"][0], cfg["prompt"][1] + 1, size=R).astype(np.int32)
+    choices = rng.integers(0, W, size=(T, R, W)).astype(np.int32)
+    init_order = rng.permutation(cfg["NB"]).astype(np.int32)
+    gen = _generator(seed, device)
+    dt, Hkv, Hq, D = cfg["dtype"], cfg["Hkv"], cfg["Hq"], cfg["D"]
+    pk = [_randn((L, int(n), Hkv, D), gen, device, dt) for n in lens]
+    pv = [_randn((L, int(n), Hkv, D), gen, device, dt) for n in lens]
+    sk = _randn((T, L, R * W, Hkv, D), gen, device, dt)
+    sv = _randn((T, L, R * W, Hkv, D), gen, device, dt)
+    q = _randn((L, R * W, Hq, D), gen, device, dt)
+    kc = torch.full((cfg["NB"], Hkv, cfg["bs"], D), float("nan"), device=device,
+                    dtype=KV_DTYPES[dt])
+    return BeamScript(seed=seed, requests=R, width=W, layers=L, Hq=Hq, Hkv=Hkv, D=D,
+                      bs=cfg["bs"], NB=cfg["NB"], dtype=dt,
+                      scale=float(np.float32(1.0 / np.sqrt(D))), steps=T, prompt_lens=lens,
+                      choices=choices, init_order=init_order, prompt_k=pk, prompt_v=pv,
+                      step_k=sk, step_v=sv, q=q, key_cache=kc, value_cache=kc.clone())
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     """Host copy of a KV-dtype tensor as its raw storage: float32 / float16 as
     themselves, bfloat16 as its uint16 bit patterns (numpy has no bfloat16)."""

@@ -209,6 +209,65 @@ def test_prefix_bad_arguments():
     assert a.prefix_evict([]) == 0 and a.prefix_size() == 1
 
 
+@pytest.mark.parametrize("seed,bs", [(0, 4), (1, 16)])
+def test_beam_churn_matches_oracle(seed, bs):
+    """Beam search without a model: every step each request's W new beams
+    pick random parents (forks for repeats, frees for beams nobody picked),
+    then every beam appends.  Slots, copy-on-write pairs, tables, reference
+    counts and the free stack agree at every step; each copy is reported for
+    exactly the beams whose last block was shared and partly filled."""
+    rng = np.random.default_rng(seed)
+    R, W, NB = 8, 8, 1024
+    order = rng.permutation(NB)
+    a = pa.Allocator(NB, bs, init_order=order)
+    o = OracleAllocator(NB, bs, init_order=order)
+    beams, nxt = [], R
+    for r in range(R):
+        n = int(rng.integers(1, 5 * bs))
+        a.create(r)
+        o.create(r)
+        assert a.append_n(r, n)[0].tolist() == [o.append(r)[0] for _ in range(n)]
+        group = [r]
+        for _ in range(W - 1):
+            a.fork(r, nxt)
+            o.fork(r, nxt)
+            group.append(nxt)
+            nxt += 1
+        beams.append(group)
+    for step in range(300):
+        new = []
+        for cur in beams:
+            pick = rng.integers(0, W, size=W)
+            used, nb = set(), []
+            for i in pick:
+                if i not in used:
+                    used.add(i)
+                    nb.append(cur[i])
+                else:
+                    a.fork(cur[i], nxt)
+                    o.fork(cur[i], nxt)
+                    nb.append(nxt)
+                    nxt += 1
+            for i, sid in enumerate(cur):
+                if i not in used:
+                    a.free(sid)
+                    o.release(sid)
+            new.append(nb)
+        beams = new
+        for sid in (b for g in beams for b in g):
+            shared_partial = o.seq_len(sid) % bs != 0 and o.ref[o.table(sid)[-1]] > 1
+            got = a.append(sid)
+            assert got == o.append(sid)
+            assert (got[1] >= 0) == shared_partial
+        state(a, o, [b for g in beams for b in g])
+    live = [b for g in beams for b in g]
+    for sid in live:
+        a.free(sid)
+        o.release(sid)
+    state(a, o, [])
+    assert a.num_free() == NB
+
+
 def rebuild(o, snap, sid):
     """The oracle applies appends one at a time; undo a partial run that hit
     out-of-blocks so both sides stay in the all-or-nothing state."""
