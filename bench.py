@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b",
                     choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix",
-                             "system_prompt"],
+                             "system_prompt", "beam"],
                     help="decode workload to time (default: the 13B-shaped batch)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
@@ -387,6 +387,116 @@ def run_shared_prefix(args, pa, synth, torch):
     return res
 
 
+BEAM_BENCH = dict(requests=16, width=4, layers=40, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16,
+                  NB=4096, prompt=(384, 640))
+
+
+def run_beam(args, pa, synth, torch):
+    """Beam search on a 40-layer, LLaMA-13B-shaped attention stack: 16
+    requests x 4 beams whose prompts are shared by their beams.  One step =
+    the beam selection (random parents: forks and frees in the allocator),
+    every beam's next slot (copy-on-write copies batched over all 40 layers
+    in one pa_copy_blocks call), then for each layer the new token's store
+    and attention.  Timed from the same starting state twice: plain fused
+    steps, and the shared-prefix path (one plan per step for all layers)."""
+    import time
+    from paged_kv_cache_198_amd import engine
+    c = dict(BEAM_BENCH)
+    R, W, L, bs = c["requests"], c["width"], c["layers"], c["bs"]
+    dt = synth.KV_DTYPES[c["dtype"]]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(args.seed)
+    rng = np.random.default_rng(args.seed)
+    plens = rng.integers(c["prompt"][0], c["prompt"][1] + 1, size=R)
+    total = args.warmup + args.steps
+    choices = rng.integers(0, W, size=(total, R, W)).tolist()
+    S = R * W
+    # values do not change the work: one random prompt, token and query set
+    pk = torch.randn(L, int(plens.max()), c["Hkv"], c["D"], generator=gen, device="cuda").to(dt)
+    nk = torch.randn(L, S, c["Hkv"], c["D"], generator=gen, device="cuda").to(dt)
+    q = torch.randn(L, S, c["Hq"], c["D"], generator=gen, device="cuda").to(dt)
+    scale = float(np.float32(1.0 / np.sqrt(c["D"])))
+    eb = synth.ELEM_BYTES[c["dtype"]]
+    row = 2 * c["Hkv"] * c["D"] * eb
+
+    def build():
+        kv = engine.PagedKV(c["NB"], bs, c["Hkv"], c["D"], c["dtype"], device="cuda", layers=L,
+                            init_order=np.random.default_rng(args.seed).permutation(c["NB"]))
+        beams, nxt = [], R
+        for r in range(R):
+            n = int(plens[r])
+            kv.prefill(r, pk[:, :n], pk[:, :n])
+            group = [r]
+            for _ in range(W - 1):
+                kv.fork(r, nxt)
+                group.append(nxt)
+                nxt += 1
+            beams.append(group)
+        return kv, beams, nxt
+
+    def run(cascade):
+        kv, beams, nxt = build()
+        torch.cuda.synchronize()
+        stats = {"copies": 0, "logical": 0, "read": 0, "host_s": 0.0}
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        for t in range(total):
+            if t == args.warmup:
+                torch.cuda.synchronize()
+                start.record()
+            h0 = time.perf_counter()
+            before = kv.copies
+            beams, nxt = engine.beam_reselect(kv, beams, choices[t], nxt)
+            flat = [b for g in beams for b in g]
+            if cascade:
+                _, plan = kv.step_cascade(q, flat, nk, nk, scale)
+                read = int((plan.items[:, 2] - plan.items[:, 1]).sum())
+            else:
+                kv.step(q, flat, nk, nk, scale)
+                read = None
+            if t >= args.warmup:
+                ctx = sum(kv.alloc.seq_len(b) for b in flat)
+                stats["copies"] += kv.copies - before
+                stats["logical"] += L * ctx * row
+                stats["read"] += L * (ctx if read is None else read) * row
+                stats["host_s"] += time.perf_counter() - h0
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        return ms, {k: v / args.steps for k, v in stats.items()}, kv
+
+    plain_ms, plain_st, kv = run(False)
+    used_plain = kv.used_blocks()
+    del kv
+    torch.cuda.empty_cache()
+    ms, st, kv = run(True)
+    gbs = lambda b, m: b / (m * 1e-3) / 1e9
+    return {
+        "metric": "beam-search decode step over 40 layers: KV GB/s (logical) + us/step",
+        "value": gbs(st["logical"], ms), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "us_per_step": ms * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c["dtype"],
+        "data": "synthetic (random K/V/q, random beam parents)",
+        "config": {"workload": f"beam search: {R} requests x {W} beams, {L} layers, "
+                               f"Hq=Hkv={c['Hkv']}, D={c['D']}, {c['dtype']}, block_size {bs}, "
+                               f"prompts uniform [{c['prompt'][0]}, {c['prompt'][1]}], "
+                               f"{c['NB']}-block pool per layer",
+                   "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": gbs(st["read"], ms), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs(st["read"], ms) / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "kernel": "whole beam step (copies + 40 x (item kernel + reduce))",
+                     "note": "achieved counts the K/V bytes the cascade must read per step"},
+        "per_step": {"cow_copies": st["copies"], "logical_kv_bytes": st["logical"],
+                     "read_kv_bytes": st["read"], "host_us": st["host_s"] * 1e6},
+        "plain_fused_step": {"us": plain_ms * 1e3, "logical_GBs": gbs(plain_st["logical"], plain_ms),
+                             "host_us": plain_st["host_s"] * 1e6,
+                             "speedup_of_cascade": plain_ms / ms},
+        "blocks_used_per_layer": {"plain_run_end": used_plain, "cascade_run_end": kv.used_blocks()},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -401,6 +511,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     pa.lib()
+    if args.workload == "beam":
+        print("[bench] beam search", file=sys.stderr, flush=True)
+        print(json.dumps(run_beam(args, pa, synth, torch)), flush=True)
+        return
     if args.workload in ("shared_prefix", "system_prompt"):
         print(f"[bench] building {args.workload} state", file=sys.stderr, flush=True)
         print(json.dumps(run_shared_prefix(args, pa, synth, torch)), flush=True)

@@ -288,10 +288,14 @@ class CascadePlan:
         return self.plan[2 * self.S:].reshape(-1, CASCADE_ITEM_INTS)
 
     def device(self, device="cuda") -> torch.Tensor:
-        """The plan as a device tensor (copied once)."""
-        if self._dev is None or str(self._dev.device) != str(torch.device(device)):
+        """The plan as a device tensor, copied once (asynchronously on the
+        current stream, through newly allocated pinned memory)."""
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if self._dev is None or self._dev.device != dev:
             src = self.plan if self.plan.size else np.zeros(1, dtype=np.int32)
-            self._dev = torch.from_numpy(src).to(device)
+            self._dev = torch.from_numpy(src).pin_memory().to(dev, non_blocking=True)
         return self._dev
 
 

@@ -21,6 +21,14 @@ import paged_kv_cache_198_amd as pa
 _DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
+def to_device(a: np.ndarray, device) -> torch.Tensor:
+    """Host array -> device tensor without waiting for the stream: staged in
+    pinned memory (newly allocated by torch's host allocator, which keeps it
+    alive until the copy has run), then copied asynchronously on the current
+    stream."""
+    return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(device, non_blocking=True)
+
+
 class PagedKV:
     """Paged K/V pools for ``layers`` attention layers that share one block
     table per sequence (a block index names the same slots in every layer's
@@ -59,7 +67,7 @@ class PagedKV:
     def _store(self, key: torch.Tensor, value: torch.Tensor, slots) -> None:
         ks, vs = self._per_layer(key), self._per_layer(value)
         assert len(ks) == self.layers
-        sl = torch.as_tensor(slots, dtype=torch.int64).to(self.device)
+        sl = to_device(np.asarray(slots, dtype=np.int64), self.device)
         for kc, vc, k, v in zip(self.key_caches, self.value_caches, ks, vs):
             pa.pa_reshape_and_cache(k.contiguous(), v.contiguous(), kc, vc, sl)
 
@@ -131,7 +139,7 @@ class PagedKV:
         if MB is None:
             MB = max(-(-self.alloc.seq_len(s) // self.bs) for s in seq_ids)
         tables, lens = self.alloc.build_batch(list(seq_ids), max(MB, 1))
-        return (torch.from_numpy(tables).to(self.device), torch.from_numpy(lens).to(self.device),
+        return (to_device(tables, self.device), to_device(lens, self.device),
                 int(lens.max()) if len(lens) else 0)
 
     def decode(self, query: torch.Tensor, seq_ids: Sequence[int], scale: float,
@@ -182,8 +190,9 @@ class PagedKV:
         out = torch.empty_like(query) if out is None else out
         outs = self._per_layer(out)
         ws = pa.make_cascade_workspace(S, Hq, self.D, plan, device=self.device)
-        tables_d = torch.from_numpy(tables).to(self.device)
-        lens_d = torch.from_numpy(lens).to(self.device)
+        tables_d = to_device(tables, self.device)
+        lens_d = to_device(lens, self.device)
+        plan.device(self.device)
         for i in range(self.layers):     # one plan serves every layer
             pa.pa_decode_cascade(outs[i], qs[i], self.key_caches[i], self.value_caches[i],
                                  tables_d, lens_d, plan, int(lens.max()) if len(lens) else 1,
