@@ -23,7 +23,8 @@ mathematics (hand-derived fixtures in ``tests/golden/``, closed forms, a dense
 library formula, invariances); none is "parity unpinned".
 
 Modules:
-  decode -- paged single-query decode attention, cache write, block copy,
-            byte accounting;
+  decode -- paged single-query decode attention, causal prefill attention
+            over a chunk of new tokens, cache write, block copy, byte
+            accounting;
   alloc  -- block allocator: free list, reference counts, copy-on-write fork.
 """

@@ -101,6 +101,50 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
     return np.stack(out) if out else np.zeros((0, Hq, D))
 
 
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                  kv_dtype: str, seqs=None) -> np.ndarray:
+    """Causal attention for a chunk of new tokens per sequence (prefill).
+
+    The pages fix only where the keys live ("PagedAttention: the KV cache was
+    the bottleneck all along", section "Virtual memory for attention": a
+    prompt's tokens go into blocks acquired as the sequence grows, and
+    attention gathers them through the block table).  Reading taken: the
+    chunk of sequence ``s`` is the last ``n = query_start[s+1] -
+    query_start[s]`` of its ``ctx = context_lens[s]`` tokens, already in the
+    pool; its token ``i`` sits at position ``p = ctx - n + i`` and attends to
+    positions ``0 .. p`` (itself included), the usual causal rule of a
+    decoder.  Rows whose position would be negative (``n > ctx``) are zero.
+
+    ``q`` is ``[T, Hq, D]`` (rows ``query_start[s] ..`` belong to ``s``), in
+    the KV dtype's storage.  Returns float64 ``[T, Hq, D]``; rows of
+    sequences not in ``seqs`` (all by default) are left zero.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    bs = k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    G = Hq // Hkv
+    sc = float(np.float32(scale))
+    S = len(context_lens)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        n, ctx = r1 - r0, int(context_lens[s])
+        if n <= 0 or ctx <= 0:
+            continue
+        K, V = gather_sequence(k_cache, v_cache, block_tables[s], ctx, bs, kv_dtype)
+        qs = widen(q[r0:r1], kv_dtype)
+        for i in range(n):
+            p = ctx - n + i
+            if p < 0:
+                continue
+            for h in range(Hq):
+                g = h // G
+                out[r0 + i, h] = attend(qs[i, h], K[:p + 1, g, :], V[:p + 1, g, :], sc)
+    return out
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, inplace=False):
     """Cache write: token ``t``'s K and V rows (``[T, Hkv, D]``) go to physical
     slot ``slot_mapping[t]`` of the pools, i.e. block ``slot // bs`` at offset

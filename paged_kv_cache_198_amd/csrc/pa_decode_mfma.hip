@@ -37,6 +37,7 @@
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
 
@@ -48,72 +49,7 @@ constexpr int kMD = 128;                   // head dim
 constexpr int kMG = 8;                     // query heads per KV head
 constexpr int kVRow = kMD * 2 + 16;        // padded LDS row of one V token (bytes)
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
-
-template <int DT>
-__device__ __forceinline__ f32x4_t mma(const u16x8_t& a, const u16x8_t& b, const f32x4_t& c) {
-  if constexpr (DT == PA_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-// float -> 16-bit pattern of the KV type (round to nearest even) and back.
-template <int DT>
-__device__ __forceinline__ uint16_t to_bits(float x) {
-  if constexpr (DT == PA_BF16) return narrow<PA_BF16>(x);
-  else return __builtin_bit_cast(uint16_t, narrow<PA_F16>(x));
-}
-template <int DT>
-__device__ __forceinline__ float from_bits(uint16_t b) {
-  if constexpr (DT == PA_BF16) return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
-  else return static_cast<float>(__builtin_bit_cast(_Float16, b));
-}
-
-__device__ __forceinline__ u16x8_t as_u16x8(const uint4& v) {
-  return __builtin_bit_cast(u16x8_t, v);
-}
-
-// bok[i] for a lane-dependent i < N (wave-uniform entries)
-template <int N>
-__device__ __forceinline__ bool pick_ok(const bool (&v)[N], int i) {
-  bool r = v[0];
-#pragma unroll
-  for (int k = 1; k < N; ++k) r = (i == k) ? v[k] : r;
-  return r;
-}
-
-// The per-wavefront LDS tile is written and read by the same wavefront,
-// whose LDS operations the hardware performs in order; this only stops the
-// compiler from moving LDS accesses across the point.
-__device__ __forceinline__ void lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // past every resource's end
-
-// Raw buffer resource over [base, base + bytes): stride 0, the gfx9 data
-// format word.  Loads at offsets >= bytes return zero and access nothing.
-__device__ __forceinline__ rsrc_t make_rsrc(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(bytes),
-                                           0x00020000);
-}
-
-// 16-byte load; K/V are read once, so the non-temporal bit is set (cache
-// policy operand: sc0 = 1, nt = 2, sc1 = 16).
-__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0,
-                                                          PA_DECODE_NT ? 2 : 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+using namespace mfma;
 
 constexpr float kLazy = 8.f;               // lazy-rescale threshold (log2 units)
 

@@ -13,6 +13,7 @@ import oracle.alloc as oa
 import oracle.decode as od
 import test_oracle_alloc as alloc_pins
 import test_oracle_pins as decode_pins
+import test_oracle_prefill_pins as prefill_pins
 
 
 # ---- decode mutants -------------------------------------------------------
@@ -158,6 +159,61 @@ def test_decode_mutant_is_caught(name, monkeypatch):
     attr, fn = DECODE_MUTANTS[name]
     monkeypatch.setattr(od, attr, fn)
     assert caught(decode_pins.PINS) is not None, f"mutant {name} passed every pin"
+
+
+# ---- prefill mutants ------------------------------------------------------
+def _prefill_with(rule):
+    """A prefill oracle whose row i of a chunk attends the key prefix
+    rule(i, n, ctx) -> end (exclusive), with heads mapped by ``head``."""
+    def fn(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, kv_dtype,
+           seqs=None, head=lambda h, G, Hkv: h // G, rows=lambda i, n: i):
+        T, Hq, D = q.shape
+        Hkv, bs = k_cache.shape[1], k_cache.shape[2]
+        G = Hq // Hkv
+        out = np.zeros((T, Hq, D))
+        for s in range(len(context_lens)):
+            r0, r1 = int(query_start[s]), int(query_start[s + 1])
+            n, ctx = r1 - r0, int(context_lens[s])
+            if n <= 0 or ctx <= 0:
+                continue
+            K, V = od.gather_sequence(k_cache, v_cache, block_tables[s], ctx, bs, kv_dtype)
+            qs = od.widen(q[r0:r1], kv_dtype)
+            for i in range(n):
+                end = rule(i, n, ctx)
+                if end <= 0:
+                    continue
+                for h in range(Hq):
+                    g = head(h, G, Hkv)
+                    out[r0 + i, h] = od.attend(qs[rows(i, n), h], K[:end, g], V[:end, g],
+                                               float(np.float32(scale)))
+        return out
+    return fn
+
+
+def _with(rule, **kw):
+    base = _prefill_with(rule)
+    return lambda *a, **k: base(*a, **{**k, **kw})
+
+
+PREFILL_MUTANTS = {
+    "causal_excludes_self": _prefill_with(lambda i, n, ctx: ctx - n + i),
+    "position_from_chunk_start": _prefill_with(lambda i, n, ctx: i + 1),
+    "not_causal": _prefill_with(lambda i, n, ctx: ctx),
+    "modulo_heads": _with(lambda i, n, ctx: ctx - n + i + 1, head=lambda h, G, Hkv: h % Hkv),
+    "rows_reversed": _with(lambda i, n, ctx: ctx - n + i + 1, rows=lambda i, n: n - 1 - i),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_prefill_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(od, "paged_prefill", PREFILL_MUTANTS[name])
+    assert caught(prefill_pins.PINS) is not None, f"mutant {name} passed every pin"
+
+
+def test_prefill_reference_rule_passes(monkeypatch):
+    # the harness itself: the correct rule written the same way passes
+    monkeypatch.setattr(od, "paged_prefill", _prefill_with(lambda i, n, ctx: ctx - n + i + 1))
+    assert caught(prefill_pins.PINS) is None
 
 
 # ---- allocator mutants ----------------------------------------------------
