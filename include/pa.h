@@ -161,6 +161,41 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
                    int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Paged prefill attention: causal attention for a chunk of new tokens per
+ * sequence ("Virtual memory for attention": a prompt's tokens fill blocks
+ * acquired as the sequence grows; attention gathers keys and values through
+ * the block table).  Sequence s's chunk is query rows
+ * query_start[s] .. query_start[s+1]; with n = that count and
+ * c = context_lens[s] (clamped to [0, MB*bs]), row i sits at position
+ * p = c - n + i and attends positions 0..p (itself included), the usual
+ * causal rule.  The chunk's own K/V must already be in the pools (store them
+ * first with pa_reshape_and_cache); earlier chunks and shared blocks are
+ * read the same way.  Rows with p < 0 get zeros.
+ *   out, query       device [T][Hq][D] of `dtype`; rows outside every
+ *                    sequence's range are not written.
+ *   key_cache,
+ *   value_cache      device [NB][Hkv][bs][D].
+ *   block_tables     device int32 [S][MB], as for pa_decode_attention.
+ *   context_lens     device int32 [S]: tokens in the pool, chunk included.
+ *   query_start      device int32 [S+1], non-decreasing, values clamped to
+ *                    [0, T].
+ *   max_query_len    host bound on every chunk's length (sizes the grid).
+ *                    A longer chunk is only partly computed: tiles run from
+ *                    its last row backwards, so its first rows are not
+ *                    written.
+ * One launch, asynchronous on `stream`, no allocation.  Supported: f16 /
+ * bf16, D = 128, Hq / Hkv in {1, 2, 4, 8}, bs in {8, 16, 32, 64, 128}; both
+ * products run on the matrix cores. */
+int pa_prefill_attention(void* out, const void* query,
+                         const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start,
+                         int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t bs, int32_t NB, int32_t MB,
+                         int32_t max_query_len, float scale,
+                         int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Shared-prefix (cascade) decode.  "Virtual memory for attention" (parallel
  * sampling, beam search): forked sequences keep pointing at the same
  * physical blocks for their common prompt, and a plain decode reads those

@@ -9,7 +9,8 @@ is no fallback: if ``libpa.so`` is missing, every call raises.
 Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_decode_attention``,
 ``pa_decode_step`` (the two fused), ``pa_decode_workspace_bytes``,
 ``pa_copy_blocks``, ``pa_cascade_plan`` / ``pa_decode_cascade`` (shared-prefix
-decode); ``Allocator`` wraps the ``pa_alloc_*`` / ``pa_seq_*``
+decode), ``pa_prefill_attention`` (causal attention over a chunk of new
+tokens); ``Allocator`` wraps the ``pa_alloc_*`` / ``pa_seq_*``
 calls.
 """
 from __future__ import annotations
@@ -57,6 +58,9 @@ _SIGNATURES = {
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                    _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t, _c_i32,
                                    _c_p]),
+    "pa_prefill_attention": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      ctypes.c_float, _c_i32, _c_p]),
     "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
                                 _c_i32, _c_i32, _c_i64, _c_p]),
     "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
@@ -253,6 +257,37 @@ def make_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_toke
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pa_prefill_attention(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, query_start: torch.Tensor,
+                         max_query_len: int, scale: float, stream=None) -> None:
+    """Causal attention for each sequence's chunk of new tokens: ``query`` and
+    ``out`` are [T, Hq, D], sequence s owning rows query_start[s] ..
+    query_start[s+1] ([S+1] int32), whose keys are the last rows of its
+    context_lens[s] tokens in the pools."""
+    dt = _kv_dtype(key_cache)
+    NB, Hkv, bs, D = key_cache.shape
+    T, Hq, Dq = query.shape
+    if Dq != D or query.dtype != key_cache.dtype:
+        raise ValueError("query must be [T, Hq, D] in the KV dtype")
+    if tuple(out.shape) != (T, Hq, D) or out.dtype != key_cache.dtype:
+        raise ValueError("out must be [T, Hq, D] in the KV dtype")
+    if value_cache.shape != key_cache.shape or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [S, MB]")
+    S, MB = block_tables.shape
+    if tuple(context_lens.shape) != (S,) or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("context_lens must be [S] and query_start [S+1]")
+    rc = lib().pa_prefill_attention(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32),
+        _dev(query_start, "query_start", torch.int32), S, T, Hq, Hkv, D, bs, NB, MB,
+        int(max_query_len), float(scale), dt, _stream(stream))
+    _check(rc, "pa_prefill_attention")
 
 
 # ---------------------------------------------------------------------------

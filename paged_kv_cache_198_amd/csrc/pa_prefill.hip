@@ -1,0 +1,329 @@
+// Paged prefill attention on the gfx950 matrix cores.
+//
+// "PagedAttention: the KV cache was the bottleneck all along", section
+// "Virtual memory for attention": a prompt's tokens go into blocks acquired
+// as the sequence grows, and attention gathers keys and values through the
+// sequence's block table.  Prefill attends a chunk of new tokens causally:
+// token i of sequence s's n-token chunk sits at position p = ctx - n + i and
+// attends positions 0..p.  The chunk's own keys and values are already in
+// the pool (written by pa_reshape_and_cache), so earlier chunks and blocks
+// shared with other sequences are read the same way.
+//
+// One workgroup of 4 wavefronts per (KV head g, sequence s, query tile).  A
+// wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
+// KV head g, each column with its own causal limit.  Per 32-token key tile:
+//   * all 256 lanes load the tile's K and V rows once (16 bytes each, raw
+//     buffer loads that return zero past a block or the range) into LDS,
+//     where the four wavefronts share them; the next tile's loads are
+//     issued before the current tile is used;
+//   * S^T = K . Q^T (2 x 4 v_mfma_f32_16x16x32): A = K rows from LDS, B = the
+//     wavefront's queries in registers; lane l then holds 8 scores of
+//     column l%16;
+//   * causal and validity masks, online softmax per column (lazy rescale as
+//     in the decode kernel);
+//   * O^T += V^T . P^T: P^T is where the scores left it, V^T is read
+//     transposed from LDS; for bf16, P goes in as a high and a low bf16 part
+//     (two products), so the probabilities keep about 16 bits.
+// Each wavefront writes its own columns' outputs: no cross-wavefront merge.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kPWaves = 4;                 // wavefronts per workgroup
+constexpr int kPTile = 32;                 // keys per tile
+constexpr int kPD = 128;                   // head dim
+constexpr int kPRow = kPD * 2 + 16;        // padded LDS row (bytes)
+constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int32_t S, T, Hq, Hkv, NB, MB;
+  float qscale;                            // scale * log2(e)
+};
+
+template <int DT, int BS, int G>
+__global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
+  using T = typename KV<DT>::T;
+  constexpr float kNegInf = -INFINITY;
+  constexpr int TPW = 16 / G;              // query tokens per wavefront
+  constexpr int QT = kPWaves * TPW;        // query tokens per workgroup
+  static_assert(BS >= 8 && (BS % 8 == 0), "block size");
+
+  __shared__ __attribute__((aligned(16))) char ks[kPTile * kPRow];
+  __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRow];
+  __shared__ int rowok[kPTile];
+
+  const int g = blockIdx.x;
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 15;                 // column
+  const int q4 = lane >> 4;                // lane group
+
+  const int r0 = min(max(a.query_start[s], 0), a.T);
+  const int r1 = min(max(a.query_start[s + 1], r0), a.T);
+  const int nq = r1 - r0;
+  const int ctx = max(0, min(a.context_lens[s], a.MB * BS));
+  const int ntiles = (nq + QT - 1) / QT;
+  if (static_cast<int>(blockIdx.z) >= ntiles) return;
+  const int qbase = (ntiles - 1 - static_cast<int>(blockIdx.z)) * QT;   // last tiles first
+
+  // this lane's column: query token qi of the chunk, query head h
+  const int qi = qbase + w * TPW + n / G;
+  const int h = g * G + n % G;
+  const int pos = ctx - nq + qi;           // its position (negative: no keys)
+  const bool col_valid = qi < nq && pos >= 0;
+  // keys the workgroup needs: up to its last query's position
+  const int last = min(qbase + QT, nq) - 1;
+  const int kend = min(ctx, ctx - nq + last + 1);
+
+  // B operand of S^T = K Q^T: lane (n, q4) holds q[column n][32kk + 8q4 .. +8]
+  u16x8_t qt[4];
+  {
+    const T* qb = static_cast<const T*>(a.q) +
+                  (static_cast<size_t>(r0 + min(qi, max(nq - 1, 0))) * a.Hq + h) * kPD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col_valid) v = *reinterpret_cast<const uint4*>(qb + 32 * kk + 8 * q4);
+      qt[kk] = as_u16x8(v);
+    }
+  }
+
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.MB;
+  const size_t bstride = static_cast<size_t>(a.Hkv) * BS * kPD * 2;
+  const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kPD * 2;
+  const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kPD * 2;
+
+  // Cooperative tile load: lane tid carries rows tid/16 and 16 + tid/16,
+  // 16-byte column tid%16.  A wavefront's four rows of one half sit in one
+  // block (bs >= 8, tiles start at multiples of 32), so the block number is
+  // wave-uniform.
+  const int lrow = tid >> 4;
+  const int lcol = tid & 15;
+  uint4 kr[2], vr[2];
+  int okr[2];
+  auto issue = [&](int t0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = t0 + lrow + 16 * j;
+      const int lb = __builtin_amdgcn_readfirstlane(min(t, max(kend - 1, 0)) / BS);
+      const int blk = __builtin_amdgcn_readfirstlane(trow[lb]);
+      const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
+      const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
+      const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
+      const rsrc_t kres = make_rsrc(kb + off, bytes);
+      const rsrc_t vres = make_rsrc(vb + off, bytes);
+      const uint32_t voff =
+          t < kend ? static_cast<uint32_t>((t % BS) * (kPD * 2) + 16 * lcol) : kOutOfRange;
+      kr[j] = buffer_load16(kres, voff);
+      vr[j] = buffer_load16(vres, voff);
+      okr[j] = bok && t < kend;
+    }
+  };
+
+  if (kend > 0) issue(0);
+  for (int t0 = 0; t0 < kend; t0 += kPTile) {
+    __syncthreads();                       // every wavefront is done with the last tile
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = lrow + 16 * j;
+      *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = kr[j];
+      *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = vr[j];
+      if (lcol == 0) rowok[r] = okr[j];
+    }
+    __syncthreads();
+    if (t0 + kPTile < kend) issue(t0 + kPTile);   // next tile's loads fly during the math
+
+    // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
+    f32x4_t sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4*>(ks + (16 * u + n) * kPRow + 64 * kk + 16 * q4);
+        sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
+      }
+    }
+    float sv[8];
+    float mt = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * u + 4 * q4 + i;
+        const bool ok = col_valid && t0 + r <= pos && rowok[r];
+        const float x = ok ? sc[u][i] * a.qscale : kNegInf;
+        sv[4 * u + i] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool bump = mt > m_run + kPLazy;
+    const float mn = bump ? mt : m_run;
+    if (__any(bump)) {
+      const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    m_run = mn;
+    // P enters the MFMA in the KV type.  bf16 keeps 8 significant bits, so a
+    // probability is split into its bf16 value and the bf16 remainder and
+    // both are multiplied in: P is then carried to about 16 bits and the
+    // output's own rounding dominates the error.  f16 (11 bits) needs no
+    // split.  The sum adds exactly the values the products use.
+    u16x8_t pb, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+      const uint16_t hi = to_bits<DT>(pv);
+      pb[jj] = hi;
+      if constexpr (DT == PA_BF16) {
+        const uint16_t lo = to_bits<DT>(pv - from_bits<DT>(hi));
+        pl[jj] = lo;
+        psum += from_bits<DT>(hi) + from_bits<DT>(lo);
+      } else {
+        psum += from_bits<DT>(hi);
+      }
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T, V^T read transposed from the shared tile
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      u16x8_t va;
+      const char* col = vs + (16 * dt + n) * 2;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int row = (jj < 4) ? 4 * q4 + jj : 16 + 4 * q4 + (jj - 4);
+        va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kPRow);
+      }
+      o[dt] = mma<DT>(va, pb, o[dt]);
+      if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
+    }
+  }
+
+  // column n's sum over the four lane groups, then this lane's four dims of
+  // each 16-dim slice
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (qi < nq) {
+    const float inv = (col_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
+    T* ob = static_cast<T*>(a.out) + (static_cast<size_t>(r0 + qi) * a.Hq + h) * kPD;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 pk;
+      pk.x = static_cast<uint32_t>(to_bits<DT>(o[dt][0] * inv)) |
+             (static_cast<uint32_t>(to_bits<DT>(o[dt][1] * inv)) << 16);
+      pk.y = static_cast<uint32_t>(to_bits<DT>(o[dt][2] * inv)) |
+             (static_cast<uint32_t>(to_bits<DT>(o[dt][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(ob + 16 * dt + 4 * q4) = pk;
+    }
+  }
+}
+
+template <int DT, int BS>
+int launch_g(const PrefillArgs& a, int G, int tiles_z, hipStream_t st) {
+  const dim3 grid(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
+                  static_cast<uint32_t>(tiles_z));
+  const dim3 block(kPWaves * 64);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<DT, BS, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<DT, BS, 2>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<DT, BS, 4>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<DT, BS, 8>), grid, block, 0, st, a); break;
+    default: return PA_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+template <int DT>
+int launch_bs(const PrefillArgs& a, int bs, int G, int tiles_z, hipStream_t st) {
+  switch (bs) {
+    case 8: return launch_g<DT, 8>(a, G, tiles_z, st);
+    case 16: return launch_g<DT, 16>(a, G, tiles_z, st);
+    case 32: return launch_g<DT, 32>(a, G, tiles_z, st);
+    case 64: return launch_g<DT, 64>(a, G, tiles_z, st);
+    case 128: return launch_g<DT, 128>(a, G, tiles_z, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_prefill_attention(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start,
+                                    int32_t S, int32_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t bs, int32_t NB, int32_t MB, int32_t max_query_len,
+                                    float scale, int32_t dtype, void* stream) {
+  if (pa::elem_bytes(dtype) == 0) return PA_ERR_INVALID;
+  if (S < 0 || T < 0 || Hq < 1 || Hkv < 1 || D < 1 || bs < 1 || NB < 1 || MB < 1)
+    return PA_ERR_INVALID;
+  if (max_query_len < 0 || Hq % Hkv || !std::isfinite(scale)) return PA_ERR_INVALID;
+  if (dtype != PA_BF16 && dtype != PA_F16) return PA_ERR_UNSUPPORTED;
+  if (D != 128) return PA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PA_ERR_UNSUPPORTED;
+  if (bs != 8 && bs != 16 && bs != 32 && bs != 64 && bs != 128) return PA_ERR_UNSUPPORTED;
+  if (S == 0 || T == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !query_start)
+    return PA_ERR_INVALID;
+  if (!pa::aligned16(out) || !pa::aligned16(query) || !pa::aligned16(key_cache) ||
+      !pa::aligned16(value_cache))
+    return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens) |
+       reinterpret_cast<uintptr_t>(query_start)) & 3u)
+    return PA_ERR_INVALID;
+  const int qt = pa::kPWaves * (16 / G);
+  const int64_t tiles = (static_cast<int64_t>(max_query_len) + qt - 1) / qt;
+  if (S > 65535 || tiles > 65535) return PA_ERR_UNSUPPORTED;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.S = S;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.NB = NB;
+  a.MB = MB;
+  a.qscale = scale * pa::kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return dtype == PA_BF16 ? pa::launch_bs<PA_BF16>(a, bs, G, static_cast<int>(tiles), st)
+                          : pa::launch_bs<PA_F16>(a, bs, G, static_cast<int>(tiles), st);
+}

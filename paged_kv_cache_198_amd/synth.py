@@ -61,9 +61,8 @@ def draw_lengths(rng: np.random.Generator, law, S: int) -> np.ndarray:
         median, sigma, lo, hi = law[1:]
         x = np.rint(np.exp(rng.normal(np.log(median), sigma, size=S)))
         x = np.clip(x, lo, hi)
-    elif kind == "fixed":
-        x = np.asarray(law[1], dtype=np.int64)
-        assert x.shape == (S,)
+    elif kind == "fixed":                 # one value for all, or one per sequence
+        x = np.broadcast_to(np.asarray(law[1], dtype=np.int64), (S,)).copy()
     else:
         raise ValueError(f"unknown length law {law!r}")
     return x.astype(np.int32)
@@ -443,6 +442,86 @@ def make_beam(seed: int = 0, device="cpu", **over) -> BeamScript:
                       scale=float(np.float32(1.0 / np.sqrt(D))), steps=T, prompt_lens=lens,
                       choices=choices, init_order=init_order, prompt_k=pk, prompt_v=pv,
                       step_k=sk, step_v=sv, q=q, key_cache=kc, value_cache=kc.clone())
+
+
+# Prefill batches: each sequence has ``prefix`` tokens already cached (an
+# earlier chunk, or blocks taken from other requests) and a chunk of new
+# tokens whose K/V are stored before the attention runs.  The default shape
+# is a LLaMA-13B attention layer with lognormal prompt lengths around the
+# pages' median, whole prompts (prefix 0).
+PREFILL = dict(S=16, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16, NB=None, pool_tokens=65536,
+               prefix=("fixed", 0), chunk=("lognormal", 700, 0.5, 16, 2048))
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    seed: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    bs: int
+    NB: int
+    dtype: str
+    scale: float
+    chunk_lens: np.ndarray       # int32 [S] new tokens per sequence
+    context_lens: np.ndarray     # int32 [S] prefix + chunk
+    query_start: np.ndarray      # int32 [S+1] packed row offsets of the chunks
+    block_tables: np.ndarray     # int32 [S, MB]
+    q: torch.Tensor              # [T, Hq, D]
+    key_cache: torch.Tensor      # [NB, Hkv, bs, D]: prefixes stored, the rest NaN
+    value_cache: torch.Tensor
+    new_key: torch.Tensor        # [T, Hkv, D] the chunks' K/V (to be stored)
+    new_value: torch.Tensor
+
+    @property
+    def T(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def MB(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    def slots(self) -> np.ndarray:
+        """Slot of every chunk row (int64 [T]), from the block tables."""
+        out = []
+        for s in range(self.S):
+            pre = int(self.context_lens[s]) - int(self.chunk_lens[s])
+            for i in range(int(self.chunk_lens[s])):
+                p = pre + i
+                out.append(int(self.block_tables[s, p // self.bs]) * self.bs + p % self.bs)
+        return np.asarray(out, dtype=np.int64)
+
+
+def make_prefill(seed: int = 0, device="cpu", **over) -> PrefillWorkload:
+    cfg = dict(PREFILL)
+    cfg.update(over)
+    S, Hq, Hkv, D, bs = cfg["S"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["bs"]
+    NB = cfg["NB"] if cfg.get("NB") else cfg["pool_tokens"] // bs
+    rng = np.random.default_rng(seed)
+    prefix = draw_lengths(rng, cfg["prefix"], S)
+    chunk = draw_lengths(rng, cfg["chunk"], S)
+    ctx = (prefix + chunk).astype(np.int32)
+    tables, _ = paged_tables(rng, ctx, bs, NB, cfg.get("MB"))
+    mask = filled_mask(tables, prefix.astype(np.int64), bs, NB)
+    gen = _generator(seed, device)
+    dt = cfg["dtype"]
+    T = int(chunk.sum())
+    q = _randn((T, Hq, D), gen, device, dt)
+    pools = []
+    poison = ~torch.from_numpy(mask).to(device)[:, None, :, None]
+    for _ in range(2):
+        p = torch.randn(NB, Hkv, bs, D, generator=gen, device=device, dtype=torch.float32)
+        p.masked_fill_(poison, float("nan"))
+        pools.append(p.to(KV_DTYPES[dt]))
+        del p
+    nk = _randn((T, Hkv, D), gen, device, dt)
+    nv = _randn((T, Hkv, D), gen, device, dt)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    return PrefillWorkload(seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
+                           scale=float(np.float32(1.0 / np.sqrt(D))), chunk_lens=chunk,
+                           context_lens=ctx, query_start=qs, block_tables=tables, q=q,
+                           key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
 
 
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:

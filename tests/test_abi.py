@@ -129,6 +129,38 @@ def test_cascade_workspace_size():
     assert pa.pa_cascade_workspace_bytes(2, 8, 128, 3) == expect
 
 
+def prefill_call(**over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, tables=FAKE, ctx=FAKE, qs=FAKE, S=2, T=10, Hq=8,
+             Hkv=2, D=128, bs=16, NB=10, MB=4, mq=8, scale=0.1, dtype=pa.PA_BF16)
+    a.update(over)
+    return pa.lib().pa_prefill_attention(
+        a["out"], a["q"], a["kc"], a["vc"], a["tables"], a["ctx"], a["qs"], a["S"], a["T"],
+        a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["mq"], a["scale"], a["dtype"],
+        None)
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(dtype=pa.PA_F32), pa.PA_ERR_UNSUPPORTED),
+    (dict(dtype=5), pa.PA_ERR_INVALID),
+    (dict(D=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(Hq=7), pa.PA_ERR_INVALID),
+    (dict(Hq=6), pa.PA_ERR_UNSUPPORTED),                 # G = 3
+    (dict(Hq=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(bs=24), pa.PA_ERR_UNSUPPORTED),
+    (dict(mq=-1), pa.PA_ERR_INVALID),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID),
+    (dict(qs=None), pa.PA_ERR_INVALID),
+    (dict(qs=FAKE + 2), pa.PA_ERR_INVALID),
+    (dict(out=FAKE + 8), pa.PA_ERR_INVALID),
+    (dict(mq=1 << 30), pa.PA_ERR_UNSUPPORTED),
+    (dict(S=0), pa.PA_OK),
+    (dict(T=0), pa.PA_OK),
+    (dict(mq=0), pa.PA_OK),
+])
+def test_prefill_argument_checks(over, expect):
+    assert prefill_call(**over) == expect
+
+
 def cache_call(**over):
     a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=3, Hkv=2, D=64, bs=16, NB=4,
              dtype=pa.PA_F16)

@@ -911,3 +911,114 @@ def test_beam_search_churn(over, cascade):
     note(f"  copies {copies}, max abs err {err:.3e}")
     assert copies > 0
     assert err <= TOL[sc.dtype]
+
+
+# ---------------------------------------------------------------------------
+# paged prefill attention: chunks of new tokens stored with
+# pa_reshape_and_cache, then attended causally (matrix cores)
+# ---------------------------------------------------------------------------
+def prefill_bound(ref, dtype):
+    """Per-element bound for prefill outputs.  The stated bound (1e-2 bf16,
+    2e-3 f16) holds while the output's own rounding stays below it, which for
+    bf16 means |out| < 4; rows near a prompt's start average few values and
+    can exceed that, and there no bf16 result can be closer than half an ulp
+    (0.0156 in [4, 8)).  So the bound is max(stated, 1.25 half-ulps of the
+    reference in the KV type)."""
+    bits = {"bf16": 8, "f16": 11, "f32": 24}[dtype]
+    a = np.maximum(np.abs(ref), 1e-30)
+    half_ulp = np.exp2(np.floor(np.log2(a)) - bits)
+    return np.maximum(TOL[dtype], 1.25 * half_ulp)
+
+
+def run_prefill_lib(w, context_lens=None, max_query_len=None):
+    lens = w.context_lens if context_lens is None else np.asarray(context_lens, dtype=np.int32)
+    kc, vc = w.key_cache.clone(), w.value_cache.clone()
+    if w.T:
+        pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc,
+                                torch.from_numpy(w.slots()).to(DEV))
+    out = torch.full((max(w.T, 1), w.Hq, w.D), float("nan"), dtype=w.q.dtype, device=DEV)[:w.T]
+    mq = int(w.chunk_lens.max()) if max_query_len is None else max_query_len
+    pa.pa_prefill_attention(out, w.q, kc, vc, torch.from_numpy(w.block_tables).to(DEV),
+                            torch.from_numpy(lens).to(DEV),
+                            torch.from_numpy(w.query_start).to(DEV), mq, w.scale)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+def prefill_oracle(w, context_lens=None, seqs=None):
+    lens = w.context_lens if context_lens is None else np.asarray(context_lens)
+    kc, vc = od.reshape_and_cache(synth.to_numpy_storage(w.new_key),
+                                  synth.to_numpy_storage(w.new_value),
+                                  synth.to_numpy_storage(w.key_cache),
+                                  synth.to_numpy_storage(w.value_cache), w.slots())
+    out = od.paged_prefill(synth.to_numpy_storage(w.q), kc, vc, w.block_tables, lens,
+                           w.query_start, w.scale, w.dtype, seqs=seqs)
+    return out, kc, vc
+
+
+PREFILL_CASES = [  # (G, Hkv, bs, dtype, prefix law, chunk law)
+    (1, 4, 16, "bf16", ("fixed", 0), ("uniform", 1, 200)),
+    (1, 4, 16, "f16", ("uniform", 0, 300), ("uniform", 1, 150)),
+    (2, 4, 8, "bf16", ("uniform", 0, 200), ("uniform", 1, 100)),
+    (4, 2, 32, "f16", ("uniform", 1, 400), ("uniform", 1, 70)),
+    (8, 2, 64, "bf16", ("uniform", 0, 700), ("uniform", 1, 90)),
+    (8, 4, 128, "bf16", ("fixed", 0), ("fixed", [1, 2, 31, 32, 33, 64])),
+    (1, 2, 128, "f16", ("fixed", [0, 127, 128, 129, 5, 1000]), ("fixed", [0, 1, 64, 65, 300, 7])),
+]
+
+
+@pytest.mark.parametrize("G,Hkv,bs,dtype,prefix,chunk", PREFILL_CASES)
+def test_prefill_against_oracle(G, Hkv, bs, dtype, prefix, chunk):
+    S = len(chunk[1]) if chunk[0] == "fixed" and np.ndim(chunk[1]) else 6
+    w = synth.make_prefill(0, device=DEV, S=S, Hq=G * Hkv, Hkv=Hkv, bs=bs, dtype=dtype,
+                           pool_tokens=32768, prefix=prefix, chunk=chunk)
+    note(f"case prefill G={G} Hkv={Hkv} bs={bs} {dtype} chunks={w.chunk_lens.tolist()} "
+         f"ctx={w.context_lens.tolist()}")
+    out, kc, vc = run_prefill_lib(w)
+    ref, rkc, rvc = prefill_oracle(w)
+    assert np.array_equal(synth.to_numpy_storage(kc).view(np.uint16), rkc.view(np.uint16))
+    assert np.array_equal(synth.to_numpy_storage(vc).view(np.uint16), rvc.view(np.uint16))
+    got = widened(out, w.dtype)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref))) if w.T else 0.0
+    note(f"  max abs err {err:.3e}, max |ref| {float(np.max(np.abs(ref))) if w.T else 0:.2f}")
+    assert (np.abs(got - ref) <= prefill_bound(ref, w.dtype)).all()
+
+
+def test_prefill_edges():
+    # chunks longer than the context (rows before position 0 are zero), a
+    # sequence with no chunk, and a grid bound tighter than one chunk: rows
+    # past the bound are left untouched
+    w = synth.make_prefill(1, device=DEV, S=4, Hq=8, Hkv=4, bs=16, pool_tokens=8192,
+                           prefix=("fixed", [0, 10, 0, 3]), chunk=("fixed", [20, 0, 5, 40]))
+    lens = w.context_lens.copy()
+    lens[0] = 12                        # 20 rows, 12 keys: the first 8 rows see nothing
+    out, _, _ = run_prefill_lib(w, context_lens=lens)
+    ref, _, _ = prefill_oracle(w, context_lens=lens)
+    got = widened(out, w.dtype)
+    assert not got[:8].any()
+    assert (np.abs(got - ref) <= prefill_bound(ref, w.dtype)).all()
+    out2, _, _ = run_prefill_lib(w, max_query_len=16)
+    got2 = widened(out2, w.dtype)
+    qs = w.query_start
+    # G = 2: a tile holds 4 x 8 = 32 query rows and tiles run last first, so
+    # one launched tile covers sequence 3's rows 32..39 of 40
+    assert np.isnan(got2[qs[3]:qs[3] + 32]).all()
+    ref2, _, _ = prefill_oracle(w)
+    for a, b in ((qs[3] + 32, qs[4]), (0, qs[3])):
+        assert (np.abs(got2[a:b] - ref2[a:b]) <= prefill_bound(ref2[a:b], w.dtype)).all()
+
+
+def test_prefill_full_size_sampled():
+    w = synth.make_prefill(0, device=DEV)
+    note(f"case prefill full: S={w.S} T={w.T} max chunk {int(w.chunk_lens.max())}")
+    out, _, _ = run_prefill_lib(w)
+    seqs = [int(np.argmax(w.chunk_lens)), int(np.argmin(w.chunk_lens)), 3]
+    ref, _, _ = prefill_oracle(w, seqs=seqs)
+    got = widened(out, w.dtype)
+    assert np.isfinite(got).all()
+    for s in seqs:
+        r0, r1 = w.query_start[s], w.query_start[s + 1]
+        err = float(np.max(np.abs(got[r0:r1] - ref[r0:r1])))
+        note(f"  sequence {s} ({r1 - r0} rows): max abs err {err:.3e}")
+        assert (np.abs(got[r0:r1] - ref[r0:r1]) <= prefill_bound(ref[r0:r1], w.dtype)).all()
