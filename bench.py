@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama13b",
                     choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix",
-                             "system_prompt", "beam"],
+                             "system_prompt", "beam", "prefill"],
                     help="decode workload to time (default: the 13B-shaped batch)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
@@ -387,6 +387,74 @@ def run_shared_prefix(args, pa, synth, torch):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / f16 matrix-core peak
+
+
+def run_prefill(args, pa, synth, torch):
+    """Prefill of a LLaMA-13B-shaped attention layer: 16 prompts with
+    lognormal lengths (median 700, in [16, 2048]), bf16, bs 16.  One step =
+    the cache write of every prompt token (pa_reshape_and_cache) + causal
+    paged attention over the prompts (pa_prefill_attention).  Algorithmic
+    flops per step = sum over prompt rows and query heads of 4 D (p + 1)
+    (two products over the p + 1 attended keys)."""
+    w = synth.make_prefill(seed=args.seed, device="cuda", bs=args.bs)
+    slots = torch.from_numpy(w.slots()).to("cuda")
+    tables = torch.from_numpy(w.block_tables).to("cuda")
+    lens = torch.from_numpy(w.context_lens).to("cuda")
+    qs = torch.from_numpy(w.query_start).to("cuda")
+    kc, vc = w.key_cache, w.value_cache
+    out = torch.empty_like(w.q)
+    mq = int(w.chunk_lens.max())
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc, slots)
+        pa.pa_prefill_attention(out, w.q, kc, vc, tables, lens, qs, mq, w.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # the attention kernel alone, between events on its stream
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(20, args.steps // 2)
+    k0.record(stream)
+    for _ in range(reps):
+        pa.pa_prefill_attention(out, w.q, kc, vc, tables, lens, qs, mq, w.scale)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = k0.elapsed_time(k1) / reps
+    flops = 0
+    for s in range(w.S):
+        n, c = int(w.chunk_lens[s]), int(w.context_lens[s])
+        keys = (c - n + 1 + c) * n // 2            # sum of (p + 1) over the chunk's rows
+        flops += 4 * w.D * w.Hq * keys
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": "prefill attention TFLOP/s (causal, algorithmic) + prompt tokens/s, "
+                  "13B-shaped layer",
+        "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "us_per_step": ms * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, lognormal prompt lengths)",
+        "config": {"workload": f"prefill: {w.S} prompts, lengths lognormal(median 700, sigma "
+                               f"0.5) in [16, 2048] ({w.T} tokens), Hq=Hkv={w.Hkv}, D={w.D}, "
+                               f"{w.dtype}, block_size {w.bs}, {w.NB}-block pool",
+                   "tokens": w.T, "seed": args.seed, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "pa::prefill_kernel (pa_prefill_attention)",
+                     "kernel_us": attn_ms * 1e3},
+        "cpu_baseline": None,
+    }
+
+
 BEAM_BENCH = dict(requests=16, width=4, layers=40, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16,
                   NB=4096, prompt=(384, 640))
 
@@ -511,6 +579,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     pa.lib()
+    if args.workload == "prefill":
+        print("[bench] prefill", file=sys.stderr, flush=True)
+        print(json.dumps(run_prefill(args, pa, synth, torch)), flush=True)
+        return
     if args.workload == "beam":
         print("[bench] beam search", file=sys.stderr, flush=True)
         print(json.dumps(run_beam(args, pa, synth, torch)), flush=True)

@@ -81,6 +81,38 @@ class PagedKV:
         self._store(key, value, slots)
         return slots
 
+    def prefill_chunks(self, seq_ids: Sequence[int], chunk_lens: Sequence[int],
+                       query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                       scale: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Prefill (or continue) existing sequences with chunks of new tokens:
+        rows of ``query`` / ``key`` / ``value`` ([T, H, D], or with a leading
+        layers axis) are the chunks packed in ``seq_ids`` order.  Each chunk
+        gets slots (copying a shared, partly filled last block first), its
+        K/V are stored in every layer, then each layer attends causally over
+        the whole context (``pa_prefill_attention``)."""
+        lens = [int(n) for n in chunk_lens]
+        slots, pairs = [], []
+        for sid, n in zip(seq_ids, lens):
+            if n == 0:
+                continue
+            sl, src, dst = self.alloc.append_n(sid, n)
+            slots.append(sl)
+            if src >= 0:
+                pairs.append((src, dst))
+        if pairs:
+            pa.pa_copy_blocks(self.key_caches, self.value_caches, pairs)
+            self.copies += len(pairs)
+        if slots:
+            self._store(key, value, np.concatenate(slots))
+        tables, ctx, _ = self.batch(seq_ids)
+        qs = to_device(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), self.device)
+        out = torch.empty_like(query) if out is None else out
+        qs_l, outs = self._per_layer(query), self._per_layer(out)
+        for i in range(self.layers):
+            pa.pa_prefill_attention(outs[i], qs_l[i], self.key_caches[i], self.value_caches[i],
+                                    tables, ctx, qs, max(lens + [0]), scale)
+        return out
+
     def publish(self, seq_id: int, keys) -> int:
         """Register the sequence's first len(keys) full blocks for reuse by
         later requests (keys name the prefix up to each block)."""
