@@ -9,7 +9,8 @@
 // the pool (written by pa_reshape_and_cache), so earlier chunks and blocks
 // shared with other sequences are read the same way.
 //
-// One workgroup of 4 wavefronts per (KV head g, sequence s, query tile).  A
+// One workgroup of 4 wavefronts per (KV head g, sequence s, query tile),
+// ordered so each XCD runs whole (s, g) pairs (see the kernel's prologue).  A
 // wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
 // KV head g, each column with its own causal limit.  Per 32-token key tile:
 //   * all 256 lanes load the tile's K and V rows once (16 bytes each, raw
@@ -55,6 +56,8 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* query_start;
   int32_t S, T, Hq, Hkv, NB, MB;
+  int32_t tiles;                           // query tiles per (sequence, KV head)
+  int32_t per_xcd;                         // workgroups per XCD
   float qscale;                            // scale * log2(e)
 };
 
@@ -70,8 +73,18 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRow];
   __shared__ int rowok[kPTile];
 
-  const int g = blockIdx.x;
-  const int s = blockIdx.y;
+  // XCD-aware order.  The hardware hands consecutive workgroups to the 8
+  // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
+  // XCD p % 8, where its query tiles, which re-read the same keys and
+  // values, run back to back on one L2; interleaving the pairs keeps the
+  // XCDs' shares of the (quadratic) causal work even.
+  const int wid = static_cast<int>(blockIdx.x);
+  const int k = wid >> 3;                  // k-th workgroup on this XCD
+  const int pair = (wid & 7) + 8 * (k / a.tiles);
+  if (pair >= a.S * a.Hkv) return;
+  const int zt = k % a.tiles;              // 0 = the pair's last (longest) tile
+  const int s = pair / a.Hkv;
+  const int g = pair - s * a.Hkv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -83,8 +96,8 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const int nq = r1 - r0;
   const int ctx = max(0, min(a.context_lens[s], a.MB * BS));
   const int ntiles = (nq + QT - 1) / QT;
-  if (static_cast<int>(blockIdx.z) >= ntiles) return;
-  const int qbase = (ntiles - 1 - static_cast<int>(blockIdx.z)) * QT;   // last tiles first
+  if (zt >= ntiles) return;
+  const int qbase = (ntiles - 1 - zt) * QT;   // last tiles first
 
   // this lane's column: query token qi of the chunk, query head h
   const int qi = qbase + w * TPW + n / G;
@@ -122,12 +135,15 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   // Cooperative tile load: lane tid carries rows tid/16 and 16 + tid/16,
   // 16-byte column tid%16.  A wavefront's four rows of one half sit in one
   // block (bs >= 8, tiles start at multiples of 32), so the block number is
-  // wave-uniform.
+  // wave-uniform.  Two register stages alternate, so a tile's loads are
+  // issued two tiles before it is used.
   const int lrow = tid >> 4;
   const int lcol = tid & 15;
-  uint4 kr[2], vr[2];
-  int okr[2];
-  auto issue = [&](int t0) {
+  struct Stage {
+    uint4 kr[2], vr[2];
+    int ok[2];
+  };
+  auto issue = [&](int t0, Stage& st) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = t0 + lrow + 16 * j;
@@ -140,95 +156,108 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       const rsrc_t vres = make_rsrc(vb + off, bytes);
       const uint32_t voff =
           t < kend ? static_cast<uint32_t>((t % BS) * (kPD * 2) + 16 * lcol) : kOutOfRange;
-      kr[j] = buffer_load16(kres, voff);
-      vr[j] = buffer_load16(vres, voff);
-      okr[j] = bok && t < kend;
+      st.kr[j] = buffer_load16(kres, voff);
+      st.vr[j] = buffer_load16(vres, voff);
+      st.ok[j] = bok && t < kend;
     }
   };
 
-  if (kend > 0) issue(0);
-  for (int t0 = 0; t0 < kend; t0 += kPTile) {
+  auto compute = [&](int t0) {
+      // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
+      f32x4_t sc[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 ka =
+              *reinterpret_cast<const uint4*>(ks + (16 * u + n) * kPRow + 64 * kk + 16 * q4);
+          sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
+        }
+      }
+      float sv[8];
+      float mt = kNegInf;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * u + 4 * q4 + i;
+          const bool ok = col_valid && t0 + r <= pos && rowok[r];
+          const float x = ok ? sc[u][i] * a.qscale : kNegInf;
+          sv[4 * u + i] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const bool bump = mt > m_run + kPLazy;
+      const float mn = bump ? mt : m_run;
+      if (__any(bump)) {
+        const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      }
+      m_run = mn;
+      // P enters the MFMA in the KV type.  bf16 keeps 8 significant bits, so a
+      // probability is split into its bf16 value and the bf16 remainder and
+      // both are multiplied in: P is then carried to about 16 bits and the
+      // output's own rounding dominates the error.  f16 (11 bits) needs no
+      // split.  The sum adds exactly the values the products use.
+      u16x8_t pb, pl;
+      float psum = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+        const uint16_t hi = to_bits<DT>(pv);
+        pb[jj] = hi;
+        if constexpr (DT == PA_BF16) {
+          const uint16_t lo = to_bits<DT>(pv - from_bits<DT>(hi));
+          pl[jj] = lo;
+          psum += from_bits<DT>(hi) + from_bits<DT>(lo);
+        } else {
+          psum += from_bits<DT>(hi);
+        }
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T, V^T read transposed from the shared tile
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        u16x8_t va;
+        const char* col = vs + (16 * dt + n) * 2;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int row = (jj < 4) ? 4 * q4 + jj : 16 + 4 * q4 + (jj - 4);
+          va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kPRow);
+        }
+        o[dt] = mma<DT>(va, pb, o[dt]);
+        if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
+      }
+  };
+
+  // one tile: publish stage `st` in LDS, refill it with the tile two ahead,
+  // then use the published tile
+  auto step = [&](int t0, Stage& st) {
     __syncthreads();                       // every wavefront is done with the last tile
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = lrow + 16 * j;
-      *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = kr[j];
-      *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = vr[j];
-      if (lcol == 0) rowok[r] = okr[j];
+      *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
+      *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = st.vr[j];
+      if (lcol == 0) rowok[r] = st.ok[j];
     }
     __syncthreads();
-    if (t0 + kPTile < kend) issue(t0 + kPTile);   // next tile's loads fly during the math
+    if (t0 + 2 * kPTile < kend) issue(t0 + 2 * kPTile, st);
+    compute(t0);
+  };
 
-    // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
-    f32x4_t sc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 ka =
-            *reinterpret_cast<const uint4*>(ks + (16 * u + n) * kPRow + 64 * kk + 16 * q4);
-        sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
-      }
-    }
-    float sv[8];
-    float mt = kNegInf;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * u + 4 * q4 + i;
-        const bool ok = col_valid && t0 + r <= pos && rowok[r];
-        const float x = ok ? sc[u][i] * a.qscale : kNegInf;
-        sv[4 * u + i] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool bump = mt > m_run + kPLazy;
-    const float mn = bump ? mt : m_run;
-    if (__any(bump)) {
-      const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    }
-    m_run = mn;
-    // P enters the MFMA in the KV type.  bf16 keeps 8 significant bits, so a
-    // probability is split into its bf16 value and the bf16 remainder and
-    // both are multiplied in: P is then carried to about 16 bits and the
-    // output's own rounding dominates the error.  f16 (11 bits) needs no
-    // split.  The sum adds exactly the values the products use.
-    u16x8_t pb, pl;
-    float psum = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
-      const uint16_t hi = to_bits<DT>(pv);
-      pb[jj] = hi;
-      if constexpr (DT == PA_BF16) {
-        const uint16_t lo = to_bits<DT>(pv - from_bits<DT>(hi));
-        pl[jj] = lo;
-        psum += from_bits<DT>(hi) + from_bits<DT>(lo);
-      } else {
-        psum += from_bits<DT>(hi);
-      }
-    }
-    l_run += psum;
-
-    // O^T += V^T P^T, V^T read transposed from the shared tile
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      u16x8_t va;
-      const char* col = vs + (16 * dt + n) * 2;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int row = (jj < 4) ? 4 * q4 + jj : 16 + 4 * q4 + (jj - 4);
-        va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kPRow);
-      }
-      o[dt] = mma<DT>(va, pb, o[dt]);
-      if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
-    }
+  Stage sa, sb;
+  if (kend > 0) issue(0, sa);
+  if (kPTile < kend) issue(kPTile, sb);
+  for (int t0 = 0; t0 < kend; t0 += 2 * kPTile) {
+    step(t0, sa);
+    if (t0 + kPTile >= kend) break;
+    step(t0 + kPTile, sb);
   }
 
   // column n's sum over the four lane groups, then this lane's four dims of
@@ -251,9 +280,8 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int DT, int BS>
-int launch_g(const PrefillArgs& a, int G, int tiles_z, hipStream_t st) {
-  const dim3 grid(static_cast<uint32_t>(a.Hkv), static_cast<uint32_t>(a.S),
-                  static_cast<uint32_t>(tiles_z));
+int launch_g(const PrefillArgs& a, int G, hipStream_t st) {
+  const dim3 grid(static_cast<uint32_t>(8 * a.per_xcd));
   const dim3 block(kPWaves * 64);
   switch (G) {
     case 1: hipLaunchKernelGGL((prefill_kernel<DT, BS, 1>), grid, block, 0, st, a); break;
@@ -266,13 +294,13 @@ int launch_g(const PrefillArgs& a, int G, int tiles_z, hipStream_t st) {
 }
 
 template <int DT>
-int launch_bs(const PrefillArgs& a, int bs, int G, int tiles_z, hipStream_t st) {
+int launch_bs(const PrefillArgs& a, int bs, int G, hipStream_t st) {
   switch (bs) {
-    case 8: return launch_g<DT, 8>(a, G, tiles_z, st);
-    case 16: return launch_g<DT, 16>(a, G, tiles_z, st);
-    case 32: return launch_g<DT, 32>(a, G, tiles_z, st);
-    case 64: return launch_g<DT, 64>(a, G, tiles_z, st);
-    case 128: return launch_g<DT, 128>(a, G, tiles_z, st);
+    case 8: return launch_g<DT, 8>(a, G, st);
+    case 16: return launch_g<DT, 16>(a, G, st);
+    case 32: return launch_g<DT, 32>(a, G, st);
+    case 64: return launch_g<DT, 64>(a, G, st);
+    case 128: return launch_g<DT, 128>(a, G, st);
     default: return PA_ERR_UNSUPPORTED;
   }
 }
@@ -307,7 +335,8 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* ke
     return PA_ERR_INVALID;
   const int qt = pa::kPWaves * (16 / G);
   const int64_t tiles = (static_cast<int64_t>(max_query_len) + qt - 1) / qt;
-  if (S > 65535 || tiles > 65535) return PA_ERR_UNSUPPORTED;
+  const int64_t units = tiles * S * Hkv;
+  if (tiles > 65535 || units > (int64_t(1) << 30)) return PA_ERR_UNSUPPORTED;
   pa::PrefillArgs a{};
   a.out = out;
   a.q = query;
@@ -322,8 +351,10 @@ extern "C" int pa_prefill_attention(void* out, const void* query, const void* ke
   a.Hkv = Hkv;
   a.NB = NB;
   a.MB = MB;
+  a.tiles = static_cast<int32_t>(tiles);
+  a.per_xcd = static_cast<int32_t>((static_cast<int64_t>(S) * Hkv + 7) / 8 * tiles);
   a.qscale = scale * pa::kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return dtype == PA_BF16 ? pa::launch_bs<PA_BF16>(a, bs, G, static_cast<int>(tiles), st)
-                          : pa::launch_bs<PA_F16>(a, bs, G, static_cast<int>(tiles), st);
+  return dtype == PA_BF16 ? pa::launch_bs<PA_BF16>(a, bs, G, st)
+                          : pa::launch_bs<PA_F16>(a, bs, G, st);
 }
