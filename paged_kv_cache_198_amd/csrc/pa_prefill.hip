@@ -22,8 +22,8 @@
 //     column l%16;
 //   * causal and validity masks, online softmax per column (lazy rescale as
 //     in the decode kernel);
-//   * O^T += V^T . P^T: P^T is where the scores left it, V^T is read
-//     transposed from LDS; for bf16, P goes in as a high and a low bf16 part
+//   * O^T += V^T . P^T: P^T is where the scores left it, V^T comes from
+//     the row-major tile through the transposing LDS read; for bf16, P goes in as a high and a low bf16 part
 //     (two products), so the probabilities keep about 16 bits.
 // Each wavefront writes its own columns' outputs: no cross-wavefront merge.
 #include <hip/hip_runtime.h>
@@ -46,6 +46,14 @@ constexpr int kPTile = 32;                 // keys per tile
 constexpr int kPD = 128;                   // head dim
 constexpr int kPRow = kPD * 2 + 16;        // padded LDS row (bytes)
 constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// LDS pointer for the transposing read (8-byte aligned)
+__device__ __forceinline__ lds_v4s_t* lds_v4s(const char* p) {
+  return (lds_v4s_t*)(const_cast<char*>(p));
+}
 
 struct PrefillArgs {
   void* out;
@@ -220,15 +228,23 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       }
       l_run += psum;
 
-      // O^T += V^T P^T, V^T read transposed from the shared tile
+      // O^T += V^T P^T.  V^T comes from the row-major V tile through the
+      // transposing LDS read (ds_read_b64_tr_b16): within a group of 16
+      // lanes, lane i receives element i%4 of the 8-byte chunks that lanes
+      // 4e + i/4 (e = 0..3) point at.  Lane j of group q4 points at key row
+      // 4*q4 + j/4, dims 16*dt + 4*(j%4), so lane i receives
+      // V[4*q4 + e][16*dt + i]: the A operand's first four entries; the same
+      // read 16 rows down gives the other four.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         u16x8_t va;
-        const char* col = vs + (16 * dt + n) * 2;
+        const char* p0 = vs + (4 * q4 + (n >> 2)) * kPRow + (16 * dt + 4 * (n & 3)) * 2;
+        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0));
+        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0 + 16 * kPRow));
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int row = (jj < 4) ? 4 * q4 + jj : 16 + 4 * q4 + (jj - 4);
-          va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kPRow);
+        for (int e = 0; e < 4; ++e) {
+          va[e] = static_cast<uint16_t>(lo[e]);
+          va[4 + e] = static_cast<uint16_t>(hi[e]);
         }
         o[dt] = mma<DT>(va, pb, o[dt]);
         if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
