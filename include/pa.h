@@ -175,7 +175,9 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
  *                    sequence's range are not written.
  *   key_cache,
  *   value_cache      device [NB][Hkv][bs][D].
- *   block_tables     device int32 [S][MB], as for pa_decode_attention.
+ *   block_tables     device int32 [S][MB].  An entry outside [0, NB) that
+ *                    falls inside the context is never dereferenced: its
+ *                    tokens count as zero keys and values.
  *   context_lens     device int32 [S]: tokens in the pool, chunk included.
  *   query_start      device int32 [S+1], non-decreasing, values clamped to
  *                    [0, T].

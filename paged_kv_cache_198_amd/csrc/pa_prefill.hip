@@ -79,7 +79,6 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) char ks[kPTile * kPRow];
   __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRow];
-  __shared__ int rowok[kPTile];
 
   // XCD-aware order.  The hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
@@ -149,7 +148,6 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const int lcol = tid & 15;
   struct Stage {
     uint4 kr[2], vr[2];
-    int ok[2];
   };
   auto issue = [&](int t0, Stage& st) {
 #pragma unroll
@@ -166,7 +164,6 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
           t < kend ? static_cast<uint32_t>((t % BS) * (kPD * 2) + 16 * lcol) : kOutOfRange;
       st.kr[j] = buffer_load16(kres, voff);
       st.vr[j] = buffer_load16(vres, voff);
-      st.ok[j] = bok && t < kend;
     }
   };
 
@@ -190,7 +187,9 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * u + 4 * q4 + i;
-          const bool ok = col_valid && t0 + r <= pos && rowok[r];
+          // rows of blocks outside the pool loaded as zeros and count as
+          // zero keys and values
+          const bool ok = col_valid && t0 + r <= pos;
           const float x = ok ? sc[u][i] * a.qscale : kNegInf;
           sv[4 * u + i] = x;
           mt = fmaxf(mt, x);
@@ -260,7 +259,6 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       const int r = lrow + 16 * j;
       *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
       *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = st.vr[j];
-      if (lcol == 0) rowok[r] = st.ok[j];
     }
     __syncthreads();
     if (t0 + 2 * kPTile < kend) issue(t0 + 2 * kPTile, st);

@@ -1009,6 +1009,35 @@ def test_prefill_edges():
         assert (np.abs(got2[a:b] - ref2[a:b]) <= prefill_bound(ref2[a:b], w.dtype)).all()
 
 
+def test_prefill_table_entry_outside_pool():
+    # an entry outside [0, NB) inside a context is never dereferenced; its
+    # tokens take part as zero keys and values (the oracle sees the same
+    # entry pointing at an all-zero block appended to its pool)
+    w = synth.make_prefill(2, device=DEV, S=3, Hq=8, Hkv=8, bs=16, pool_tokens=4096,
+                           prefix=("fixed", [40, 0, 70]), chunk=("fixed", [20, 50, 9]))
+    bad = w.block_tables.copy()
+    bad[0, 1] = w.NB + 3
+    bad[2, 0] = -7
+    kc, vc = w.key_cache.clone(), w.value_cache.clone()
+    pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc, torch.from_numpy(w.slots()).to(DEV))
+    out = torch.empty_like(w.q)
+    pa.pa_prefill_attention(out, w.q, kc, vc, torch.from_numpy(bad).to(DEV),
+                            torch.from_numpy(w.context_lens).to(DEV),
+                            torch.from_numpy(w.query_start).to(DEV), int(w.chunk_lens.max()),
+                            w.scale)
+    torch.cuda.synchronize()
+    okc = synth.to_numpy_storage(kc)
+    ovc = synth.to_numpy_storage(vc)
+    zero = np.zeros((1,) + okc.shape[1:], dtype=okc.dtype)
+    okc, ovc = np.concatenate([okc, zero]), np.concatenate([ovc, zero])
+    tab = bad.copy()
+    tab[0, 1] = tab[2, 0] = w.NB
+    ref = od.paged_prefill(synth.to_numpy_storage(w.q), okc, ovc, tab, w.context_lens,
+                           w.query_start, w.scale, w.dtype)
+    got = widened(out, w.dtype)
+    assert (np.abs(got - ref) <= prefill_bound(ref, w.dtype)).all()
+
+
 def test_prefill_full_size_sampled():
     w = synth.make_prefill(0, device=DEV)
     note(f"case prefill full: S={w.S} T={w.T} max chunk {int(w.chunk_lens.max())}")
