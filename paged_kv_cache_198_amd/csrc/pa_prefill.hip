@@ -23,8 +23,9 @@
 //   * causal and validity masks, online softmax per column (lazy rescale as
 //     in the decode kernel);
 //   * O^T += V^T . P^T: P^T is where the scores left it, V^T comes from
-//     the row-major tile through the transposing LDS read; for bf16, P goes in as a high and a low bf16 part
-//     (two products), so the probabilities keep about 16 bits.
+//     the row-major tile through the transposing LDS read; for bf16, P goes
+//     in as its top 16 bits plus the top 16 bits of the remainder (two
+//     products), so the probabilities keep about 15 bits.
 // Each wavefront writes its own columns' outputs: no cross-wavefront merge.
 #include <hip/hip_runtime.h>
 
@@ -205,23 +206,42 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
         for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
       }
       m_run = mn;
-      // P enters the MFMA in the KV type.  bf16 keeps 8 significant bits, so a
-      // probability is split into its bf16 value and the bf16 remainder and
-      // both are multiplied in: P is then carried to about 16 bits and the
-      // output's own rounding dominates the error.  f16 (11 bits) needs no
-      // split.  The sum adds exactly the values the products use.
+      // P enters the MFMA in the KV type.  f16 keeps 11 significant bits
+      // and is rounded to nearest.  bf16 keeps 8, so each probability goes
+      // in as two bf16 parts: its top 16 bits (truncation) and the top 16
+      // bits of the exact remainder; both are multiplied in, carrying P to
+      // about 15 bits, and the sum adds exactly the values the products
+      // use.  Truncation makes each part a bit mask and a byte permute.
       u16x8_t pb, pl;
       float psum = 0.f;
+      if constexpr (DT == PA_BF16) {
+        uint32_t hb[8], lb[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
-        const uint16_t hi = to_bits<DT>(pv);
-        pb[jj] = hi;
-        if constexpr (DT == PA_BF16) {
-          const uint16_t lo = to_bits<DT>(pv - from_bits<DT>(hi));
-          pl[jj] = lo;
-          psum += from_bits<DT>(hi) + from_bits<DT>(lo);
-        } else {
+        for (int jj = 0; jj < 8; ++jj) {
+          const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+          const uint32_t b = __builtin_bit_cast(uint32_t, pv);
+          const float hf = __builtin_bit_cast(float, b & 0xffff0000u);
+          const uint32_t r = __builtin_bit_cast(uint32_t, pv - hf);   // exact
+          const float lf = __builtin_bit_cast(float, r & 0xffff0000u);
+          hb[jj] = b;
+          lb[jj] = r;
+          psum += hf + lf;
+        }
+        // upper halves of two words into one: byte selector 0x07060302
+        uint32_t ph[4], pq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ph[k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
+          pq[k] = __builtin_amdgcn_perm(lb[2 * k + 1], lb[2 * k], 0x07060302u);
+        }
+        pb = __builtin_bit_cast(u16x8_t, ph);
+        pl = __builtin_bit_cast(u16x8_t, pq);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+          const uint16_t hi = to_bits<DT>(pv);
+          pb[jj] = hi;
           psum += from_bits<DT>(hi);
         }
       }
@@ -236,15 +256,11 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // read 16 rows down gives the other four.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        u16x8_t va;
         const char* p0 = vs + (4 * q4 + (n >> 2)) * kPRow + (16 * dt + 4 * (n & 3)) * 2;
         const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0));
         const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0 + 16 * kPRow));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          va[e] = static_cast<uint16_t>(lo[e]);
-          va[4 + e] = static_cast<uint16_t>(hi[e]);
-        }
+        const u16x8_t va =
+            __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = mma<DT>(va, pb, o[dt]);
         if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
       }
