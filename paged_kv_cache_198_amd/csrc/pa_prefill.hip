@@ -181,17 +181,17 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
           sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
         }
       }
+      // Causal mask; rows of blocks outside the pool were loaded as zeros
+      // and count as zero keys and values.
       float sv[8];
       float mt = kNegInf;
+      const int lim = col_valid ? pos - t0 : -1;   // rows r <= lim take part
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * u + 4 * q4 + i;
-          // rows of blocks outside the pool loaded as zeros and count as
-          // zero keys and values
-          const bool ok = col_valid && t0 + r <= pos;
-          const float x = ok ? sc[u][i] * a.qscale : kNegInf;
+          const float x = r <= lim ? sc[u][i] * a.qscale : kNegInf;
           sv[4 * u + i] = x;
           mt = fmaxf(mt, x);
         }
@@ -212,13 +212,16 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // bits of the exact remainder; both are multiplied in, carrying P to
       // about 15 bits, and the sum adds exactly the values the products
       // use.  Truncation makes each part a bit mask and a byte permute.
+      // a finite reference: while no key has taken part (mn = -inf) every
+      // score is -inf and exp2(-inf - 0) = 0
+      const float mref = mn == kNegInf ? 0.f : mn;
       u16x8_t pb, pl;
       float psum = 0.f;
       if constexpr (DT == PA_BF16) {
         uint32_t hb[8], lb[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+          const float pv = fast_exp2(sv[jj] - mref);        // exp2(-inf) = 0
           const uint32_t b = __builtin_bit_cast(uint32_t, pv);
           const float hf = __builtin_bit_cast(float, b & 0xffff0000u);
           const uint32_t r = __builtin_bit_cast(uint32_t, pv - hf);   // exact
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       } else {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
+          const float pv = fast_exp2(sv[jj] - mref);
           const uint16_t hi = to_bits<DT>(pv);
           pb[jj] = hi;
           psum += from_bits<DT>(hi);
