@@ -26,8 +26,8 @@
 //     the accumulators are rarely rescaled.
 //   * O^T += V^T . P^T: B = P^T is already where the scores left it (lane l:
 //     head l%16, the 8 tokens 4(l/16)+i and 16+4(l/16)+i), A = V^T comes from
-//     the same LDS tile, now holding the V rows (rows padded to 272 bytes, so
-//     the 4 lane groups read disjoint banks).  The output rows of O^T are dims
+//     the same LDS tile, now holding the V rows (rows padded to 272 bytes),
+//     through the transposing LDS read (two 8-byte reads per 16 dims).  The output rows of O^T are dims
 //     and its columns heads, so lane l holds head l%16: the per-head rescale
 //     factor never leaves the lane.
 // Probabilities enter the second product rounded to the KV type; the running
@@ -309,16 +309,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
       *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
     lds_order();
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      u16x8_t va;
-      const char* col = vt + (16 * dt + n) * 2;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int row = (jj < 4) ? 4 * q + jj : 16 + 4 * q + (jj - 4);
-        va[jj] = *reinterpret_cast<const uint16_t*>(col + row * kVRow);
-      }
-      o[dt] = mma<DT>(va, pb, o[dt]);
-    }
+    for (int dt = 0; dt < 8; ++dt) o[dt] = mma<DT>(vt_operand(vt, kVRow, dt, n, q), pb, o[dt]);
     lds_order();                           // the next tile rewrites these rows
   };
 

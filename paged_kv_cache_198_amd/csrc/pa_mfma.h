@@ -78,5 +78,29 @@ __device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t voff) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element i%4 (16-bit) of the 8-byte chunks that the
+// group's lanes 4e + i/4 (e = 0..3) point at.  For a row-major tile
+// (token rows, 16-bit dims), lane j of group q pointing at row 4q + j/4,
+// dims c + 4(j%4), gives lane i the values of dim c + i in rows 4q .. 4q+3:
+// an MFMA operand column read across token rows.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+__device__ __forceinline__ v4s_t ds_read_tr16(const char* p) {   // p: LDS, 8-byte aligned
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(const_cast<char*>(p)));
+}
+
+// A operand of O^T += V^T P^T from a row-major 32-row tile of 16-bit rows
+// (row stride `stride` bytes): lane (n, q) gets dims 16dt + n of rows
+// 4q .. 4q+3 and 16+4q .. 16+4q+3 (the order the score tile leaves P^T in).
+__device__ __forceinline__ u16x8_t vt_operand(const char* tile, int stride, int dt, int n,
+                                              int q) {
+  const char* p0 = tile + (4 * q + (n >> 2)) * stride + (16 * dt + 4 * (n & 3)) * 2;
+  const v4s_t lo = ds_read_tr16(p0);
+  const v4s_t hi = ds_read_tr16(p0 + 16 * stride);
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 }  // namespace mfma
 }  // namespace pa

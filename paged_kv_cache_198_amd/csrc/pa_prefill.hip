@@ -48,13 +48,6 @@ constexpr int kPD = 128;                   // head dim
 constexpr int kPRow = kPD * 2 + 16;        // padded LDS row (bytes)
 constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
 
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
-
-// LDS pointer for the transposing read (8-byte aligned)
-__device__ __forceinline__ lds_v4s_t* lds_v4s(const char* p) {
-  return (lds_v4s_t*)(const_cast<char*>(p));
-}
 
 struct PrefillArgs {
   void* out;
@@ -259,11 +252,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // read 16 rows down gives the other four.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const char* p0 = vs + (4 * q4 + (n >> 2)) * kPRow + (16 * dt + 4 * (n & 3)) * 2;
-        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0));
-        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4s(p0 + 16 * kPRow));
-        const u16x8_t va =
-            __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u16x8_t va = vt_operand(vs, kPRow, dt, n, q4);
         o[dt] = mma<DT>(va, pb, o[dt]);
         if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
       }
