@@ -203,8 +203,9 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // and is rounded to nearest.  bf16 keeps 8, so each probability goes
       // in as two bf16 parts: its top 16 bits (truncation) and the top 16
       // bits of the exact remainder; both are multiplied in, carrying P to
-      // about 15 bits, and the sum adds exactly the values the products
-      // use.  Truncation makes each part a bit mask and a byte permute.
+      // about 15 bits; the sum adds pv itself (the parts differ from it by
+      // under 2^-14 relative).  Truncation makes each part a bit mask and a
+      // byte permute.
       // a finite reference: while no key has taken part (mn = -inf) every
       // score is -inf and exp2(-inf - 0) = 0
       const float mref = mn == kNegInf ? 0.f : mn;
@@ -217,11 +218,9 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
           const float pv = fast_exp2(sv[jj] - mref);        // exp2(-inf) = 0
           const uint32_t b = __builtin_bit_cast(uint32_t, pv);
           const float hf = __builtin_bit_cast(float, b & 0xffff0000u);
-          const uint32_t r = __builtin_bit_cast(uint32_t, pv - hf);   // exact
-          const float lf = __builtin_bit_cast(float, r & 0xffff0000u);
           hb[jj] = b;
-          lb[jj] = r;
-          psum += hf + lf;
+          lb[jj] = __builtin_bit_cast(uint32_t, pv - hf);   // exact remainder
+          psum += pv;   // the two parts carry pv to within 2^-14 of itself
         }
         // upper halves of two words into one: byte selector 0x07060302
         uint32_t ph[4], pq[4];
