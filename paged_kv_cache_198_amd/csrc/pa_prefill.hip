@@ -133,27 +133,29 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kPD * 2;
   const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kPD * 2;
 
-  // Cooperative tile load: lane tid carries rows tid/16 and 16 + tid/16,
-  // 16-byte column tid%16.  A wavefront's four rows of one half sit in one
-  // block (bs >= 8, tiles start at multiples of 32), so the block number is
-  // wave-uniform.  Two register stages alternate, so a tile's loads are
-  // issued two tiles before it is used.
-  const int lrow = tid >> 4;
-  const int lcol = tid & 15;
+  // Cooperative tile load: wavefront w carries rows 8w .. 8w+7 (lane l:
+  // rows 8w + l/16 and 8w + 4 + l/16, 16-byte column l%16).  The eight rows
+  // sit in one block (bs >= 8, tiles start at multiples of 32), so one table
+  // entry and one buffer resource per pool serve the wavefront.  Two
+  // register stages alternate, so a tile's loads are issued two tiles
+  // before it is used.
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  const int lrow = 8 * wv + (lane >> 4);
+  const int lcol = lane & 15;
   struct Stage {
     uint4 kr[2], vr[2];
   };
   auto issue = [&](int t0, Stage& st) {
+    const int lb = min(t0 + 8 * wv, max(kend - 1, 0)) / BS;   // wave-uniform
+    const int blk = trow[lb];
+    const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
+    const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
+    const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
+    const rsrc_t kres = make_rsrc(kb + off, bytes);
+    const rsrc_t vres = make_rsrc(vb + off, bytes);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int t = t0 + lrow + 16 * j;
-      const int lb = __builtin_amdgcn_readfirstlane(min(t, max(kend - 1, 0)) / BS);
-      const int blk = __builtin_amdgcn_readfirstlane(trow[lb]);
-      const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
-      const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
-      const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
-      const rsrc_t kres = make_rsrc(kb + off, bytes);
-      const rsrc_t vres = make_rsrc(vb + off, bytes);
+      const int t = t0 + lrow + 4 * j;
       const uint32_t voff =
           t < kend ? static_cast<uint32_t>((t % BS) * (kPD * 2) + 16 * lcol) : kOutOfRange;
       st.kr[j] = buffer_load16(kres, voff);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     __syncthreads();                       // every wavefront is done with the last tile
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int r = lrow + 16 * j;
+      const int r = lrow + 4 * j;
       *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
       *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = st.vr[j];
     }
