@@ -75,10 +75,12 @@ __device__ __forceinline__ typename KV<DT>::T narrow(float x) {
   } else if constexpr (DT == PA_F16) {
     return static_cast<_Float16>(x);
   } else {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    // round to nearest even; a NaN stays a (quiet) NaN.  Both results are
+    // formed and one selected, so no lane branches.
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = (u >> 16) | 0x40u;
+    return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
   }
 }
 

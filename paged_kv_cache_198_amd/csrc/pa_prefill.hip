@@ -155,9 +155,12 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     const rsrc_t vres = make_rsrc(vb + off, bytes);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int t = t0 + lrow + 4 * j;
-      const uint32_t voff =
-          t < kend ? static_cast<uint32_t>((t % BS) * (kPD * 2) + 16 * lcol) : kOutOfRange;
+      // row within its block: t0 is a multiple of 32, so for bs <= 32 it is
+      // the lane's tile row mod bs, else the tile's offset plus that row
+      const uint32_t r = static_cast<uint32_t>(lrow + 4 * j);
+      const uint32_t rib = BS > kPTile ? (static_cast<uint32_t>(t0) & (BS - 1)) + r : r & (BS - 1);
+      const uint32_t in = rib * (kPD * 2) + 16u * static_cast<uint32_t>(lcol);
+      const uint32_t voff = t0 + static_cast<int>(r) < kend ? in : kOutOfRange;
       st.kr[j] = buffer_load16(kres, voff);
       st.vr[j] = buffer_load16(vres, voff);
     }
