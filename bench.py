@@ -218,6 +218,25 @@ def cpu_baseline(step, budget_s=10.0):
                       f"passes, {secs:.1f} s, float64 numpy"}
 
 
+def read_probe(pa, torch, nbytes, reps=10):
+    """The library's plain streaming-read kernel over ``nbytes``: the read
+    rate this machine reaches with the decode kernels' loads and no math."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    out = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    pa.pa_probe_read_bandwidth(src, out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        pa.pa_probe_read_bandwidth(src, out)
+    e.record()
+    torch.cuda.synchronize()
+    rate = (nbytes // 2) * 2 * reps / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, out
+    torch.cuda.empty_cache()
+    return rate
+
+
 def hbm_probe(torch, gib=4, reps=10):
     """Plain device-memory rates on this machine from torch's own kernels: a copy
     (read + write) and a sum (read only) over ``gib`` GiB; context for the
@@ -661,6 +680,13 @@ def main():
     }
     if not args.no_probe:
         line["hbm_probe"] = hbm_probe(torch)
+        # the practical ceiling: a plain streaming read of the decode's byte
+        # count, and of 4 GiB
+        alg = line["roofline"]["algorithmic_bytes_per_launch"]
+        same = read_probe(pa, torch, int(alg) // 16 * 16)
+        big = read_probe(pa, torch, 4 << 30)
+        line["hbm_probe"]["pa_read_probe_GBs"] = {"same_bytes": same, "4GiB": big}
+        line["roofline"]["frac_of_read_probe"] = line["roofline"]["achieved"] / same
     if args.calibrate_copy:
         calibrate_copy(torch)
     if not args.no_cpu_baseline:

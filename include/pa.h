@@ -284,6 +284,18 @@ int pa_decode_cascade(void* out, const void* query, const void* key, const void*
                       int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Diagnostic, not part of the path: reads `bytes` (a multiple of 16) of
+ * device memory at `src` with the decode kernels' 16-byte non-temporal loads
+ * in a grid-stride loop, so a timed call measures the read rate a plain
+ * streaming kernel reaches on this GPU (the practical ceiling the decode
+ * kernels' fraction of the nominal peak is read against).  Each thread
+ * stores one folded word into out (device, out_words >= 256; the launch uses
+ * min(out_words / 256, 4096) workgroups of 256 threads).  Asynchronous on
+ * `stream`. */
+int pa_probe_read_bandwidth(const void* src, size_t bytes, uint32_t* out, int32_t out_words,
+                            void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Block copy for copy-on-write ("Virtual memory for attention": a completion
  * that diverges from a shared block gets its own copy).  For every pair
  * (src, dst) and every layer l, key block dst becomes a copy of key block

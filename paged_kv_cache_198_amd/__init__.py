@@ -61,6 +61,7 @@ _SIGNATURES = {
     "pa_prefill_attention": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                       ctypes.c_float, _c_i32, _c_p]),
+    "pa_probe_read_bandwidth": (_c_int, [_c_p, ctypes.c_size_t, _c_p, _c_i32, _c_p]),
     "pa_copy_blocks": (_c_int, [ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_i32, _p_i64,
                                 _c_i32, _c_i32, _c_i64, _c_p]),
     "pa_alloc_create": (_c_p, [_c_i32, _c_i32, _p_i32]),
@@ -410,6 +411,16 @@ def pa_decode_cascade(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
         int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
         _stream(stream))
     _check(rc, "pa_decode_cascade")
+
+
+def pa_probe_read_bandwidth(src: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Diagnostic streaming read of all of ``src`` (device, any dtype, size a
+    multiple of 16 bytes); ``out`` is a device int32 buffer of at least 256
+    words that receives one folded word per thread."""
+    nbytes = src.numel() * src.element_size()
+    rc = lib().pa_probe_read_bandwidth(_dev(src, "src"), nbytes, _dev(out, "out", torch.int32),
+                                       out.numel(), _stream(stream))
+    _check(rc, "pa_probe_read_bandwidth")
 
 
 def pa_copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],

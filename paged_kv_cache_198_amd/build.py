@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_abi.cpp", "pa_alloc.cpp", "pa_cascade.cpp", "pa_cache_ops.hip", "pa_decode.hip",
-           "pa_decode_mfma.hip", "pa_prefill.hip"]
+           "pa_decode_mfma.hip", "pa_prefill.hip", "pa_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-result"]

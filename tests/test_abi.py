@@ -161,6 +161,15 @@ def test_prefill_argument_checks(over, expect):
     assert prefill_call(**over) == expect
 
 
+def test_read_probe_argument_checks():
+    f = pa.lib().pa_probe_read_bandwidth
+    assert f(None, 1 << 20, FAKE, 4096, None) == pa.PA_ERR_INVALID
+    assert f(FAKE, 100, FAKE, 4096, None) == pa.PA_ERR_INVALID        # not a multiple of 16
+    assert f(FAKE + 8, 1 << 20, FAKE, 4096, None) == pa.PA_ERR_INVALID
+    assert f(FAKE, 1 << 20, FAKE, 255, None) == pa.PA_ERR_INVALID      # room for one workgroup
+    assert f(FAKE, 1 << 20, FAKE + 2, 4096, None) == pa.PA_ERR_INVALID
+
+
 def cache_call(**over):
     a = dict(k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=3, Hkv=2, D=64, bs=16, NB=4,
              dtype=pa.PA_F16)

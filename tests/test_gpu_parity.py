@@ -1127,3 +1127,18 @@ def test_engine_chunked_prefill_with_registry():
     assert np.array_equal(synth.to_numpy_storage(kv.key_cache).view(np.uint16), okc.view(np.uint16))
     assert np.array_equal(synth.to_numpy_storage(kv.value_cache).view(np.uint16), ovc.view(np.uint16))
     assert kv.alloc.export() == (list(oa_.ref), oa_.free_stack())
+
+
+def test_read_probe_reads_every_chunk():
+    # 1 MiB = 65536 chunks of 16 bytes, 4096 x 256 threads: thread t reads
+    # chunk t (if any) and stores the XOR of its four words
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    src = torch.randint(-2**31, 2**31 - 1, (1 << 18,), generator=g, device=DEV, dtype=torch.int32)
+    out = torch.full((4096 * 256,), -1, dtype=torch.int32, device=DEV)
+    pa.pa_probe_read_bandwidth(src, out)
+    torch.cuda.synchronize()
+    w = src.cpu().numpy().view(np.uint32).reshape(-1, 4)
+    expect = np.zeros(4096 * 256, dtype=np.uint32)
+    expect[:w.shape[0]] = w[:, 0] ^ w[:, 1] ^ w[:, 2] ^ w[:, 3]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), expect)
