@@ -45,7 +45,12 @@ using namespace mfma;
 constexpr int kPWaves = 4;                 // wavefronts per workgroup
 constexpr int kPTile = 32;                 // keys per tile
 constexpr int kPD = 128;                   // head dim
-constexpr int kPRow = kPD * 2 + 16;        // padded LDS row (bytes)
+// Padded LDS rows.  K rows (68 dwords) let the 16 lanes of an operand read
+// (rows n = 0..15, 16 bytes each) hit 16 distinct bank groups; V rows (72
+// dwords) let the transposing read's four rows of 8 dwords per 16-lane
+// group fall on disjoint banks.  No single stride does both.
+constexpr int kPRow = kPD * 2 + 16;        // K
+constexpr int kPRowV = kPD * 2 + 32;       // V
 constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
 
 
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   static_assert(BS >= 8 && (BS % 8 == 0), "block size");
 
   __shared__ __attribute__((aligned(16))) char ks[kPTile * kPRow];
-  __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRow];
+  __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRowV];
 
   // XCD-aware order.  The hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // read 16 rows down gives the other four.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u16x8_t va = vt_operand(vs, kPRow, dt, n, q4);
+        const u16x8_t va = vt_operand(vs, kPRowV, dt, n, q4);
         o[dt] = mma<DT>(va, pb, o[dt]);
         if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
       }
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int r = lrow + 4 * j;
       *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
-      *reinterpret_cast<uint4*>(vs + r * kPRow + 16 * lcol) = st.vr[j];
+      *reinterpret_cast<uint4*>(vs + r * kPRowV + 16 * lcol) = st.vr[j];
     }
     __syncthreads();
     if (t0 + 2 * kPTile < kend) issue(t0 + 2 * kPTile, st);
