@@ -9,13 +9,13 @@
 // the pool (written by pa_reshape_and_cache), so earlier chunks and blocks
 // shared with other sequences are read the same way.
 //
-// One workgroup of 4 wavefronts per (KV head g, sequence s, query tile),
+// One workgroup of 8 wavefronts per (KV head g, sequence s, query tile),
 // ordered so each XCD runs whole (s, g) pairs (see the kernel's prologue).  A
 // wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
 // KV head g, each column with its own causal limit.  Per 32-token key tile:
-//   * all 256 lanes load the tile's K and V rows once (16 bytes each, raw
+//   * all 512 lanes load the tile's K and V rows once (16 bytes each, raw
 //     buffer loads that return zero past a block or the range) into LDS,
-//     where the four wavefronts share them; the next tile's loads are
+//     where the eight wavefronts share them; the next tiles' loads are
 //     issued before the current tile is used;
 //   * S^T = K . Q^T (2 x 4 v_mfma_f32_16x16x32): A = K rows from LDS, B = the
 //     wavefront's queries in registers; lane l then holds 8 scores of
@@ -42,7 +42,8 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kPWaves = 4;                 // wavefronts per workgroup
+constexpr int kPWaves = 8;                 // wavefronts per workgroup
+constexpr int kPRowsW = 32 / kPWaves;      // tile rows each wavefront loads
 constexpr int kPTile = 32;                 // keys per tile
 constexpr int kPD = 128;                   // head dim
 // Padded LDS rows.  K rows (68 dwords) let the 16 lanes of an operand read
@@ -113,6 +114,11 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   // keys the workgroup needs: up to its last query's position
   const int last = min(qbase + QT, nq) - 1;
   const int kend = min(ctx, ctx - nq + last + 1);
+  // the last position this wavefront's columns attend: key tiles past it
+  // are masked out for all its columns and are skipped (they would add
+  // zero probability and leave the running max alone)
+  const int wlast = qbase + w * TPW < nq ? ctx - nq + min(qbase + w * TPW + TPW, nq) - 1 : -1;
+  const int wend = __builtin_amdgcn_readfirstlane(wlast);
 
   // B operand of S^T = K Q^T: lane (n, q4) holds q[column n][32kk + 8q4 .. +8]
   u16x8_t qt[4];
@@ -138,20 +144,20 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kPD * 2;
   const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kPD * 2;
 
-  // Cooperative tile load: wavefront w carries rows 8w .. 8w+7 (lane l:
-  // rows 8w + l/16 and 8w + 4 + l/16, 16-byte column l%16).  The eight rows
-  // sit in one block (bs >= 8, tiles start at multiples of 32), so one table
-  // entry and one buffer resource per pool serve the wavefront.  Two
-  // register stages alternate, so a tile's loads are issued two tiles
-  // before it is used.
+  // Cooperative tile load: wavefront w carries rows 4w .. 4w+3 (lane l: row
+  // 4w + l/16, 16-byte column l%16).  The four rows sit in one block (bs >= 8,
+  // tiles start at multiples of 32), so one table entry and one buffer
+  // resource per pool serve the wavefront.  Two register stages alternate,
+  // so a tile's loads are issued two tiles before it is used.
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  const int lrow = 8 * wv + (lane >> 4);
+  constexpr int NJ = kPRowsW / 4;          // 16-lane row groups per wavefront
+  const int lrow = kPRowsW * wv + (lane >> 4);
   const int lcol = lane & 15;
   struct Stage {
-    uint4 kr[2], vr[2];
+    uint4 kr[NJ], vr[NJ];
   };
   auto issue = [&](int t0, Stage& st) {
-    const int lb = min(t0 + 8 * wv, max(kend - 1, 0)) / BS;   // wave-uniform
+    const int lb = min(t0 + kPRowsW * wv, max(kend - 1, 0)) / BS;   // wave-uniform
     const int blk = trow[lb];
     const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
     const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     const rsrc_t kres = make_rsrc(kb + off, bytes);
     const rsrc_t vres = make_rsrc(vb + off, bytes);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       // row within its block: t0 is a multiple of 32, so for bs <= 32 it is
       // the lane's tile row mod bs, else the tile's offset plus that row
       const uint32_t r = static_cast<uint32_t>(lrow + 4 * j);
@@ -272,14 +278,14 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   auto step = [&](int t0, Stage& st) {
     __syncthreads();                       // every wavefront is done with the last tile
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int r = lrow + 4 * j;
       *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
       *reinterpret_cast<uint4*>(vs + r * kPRowV + 16 * lcol) = st.vr[j];
     }
     __syncthreads();
     if (t0 + 2 * kPTile < kend) issue(t0 + 2 * kPTile, st);
-    compute(t0);
+    if (t0 <= wend) compute(t0);
   };
 
   Stage sa, sb;

@@ -990,7 +990,7 @@ def test_prefill_edges():
     # sequence with no chunk, and a grid bound tighter than one chunk: rows
     # past the bound are left untouched
     w = synth.make_prefill(1, device=DEV, S=4, Hq=8, Hkv=4, bs=16, pool_tokens=8192,
-                           prefix=("fixed", [0, 10, 0, 3]), chunk=("fixed", [20, 0, 5, 40]))
+                           prefix=("fixed", [0, 10, 0, 3]), chunk=("fixed", [20, 0, 5, 80]))
     lens = w.context_lens.copy()
     lens[0] = 12                        # 20 rows, 12 keys: the first 8 rows see nothing
     out, _, _ = run_prefill_lib(w, context_lens=lens)
@@ -1001,11 +1001,12 @@ def test_prefill_edges():
     out2, _, _ = run_prefill_lib(w, max_query_len=16)
     got2 = widened(out2, w.dtype)
     qs = w.query_start
-    # G = 2: a tile holds 4 x 8 = 32 query rows and tiles run last first, so
-    # one launched tile covers sequence 3's rows 32..39 of 40
-    assert np.isnan(got2[qs[3]:qs[3] + 32]).all()
+    # G = 2: a tile holds 8 wavefronts x 8 = 64 query rows, tiles start at
+    # multiples of 64 and run last first, so one launched tile covers
+    # sequence 3's rows 64..79 of 80
+    assert np.isnan(got2[qs[3]:qs[3] + 64]).all()
     ref2, _, _ = prefill_oracle(w)
-    for a, b in ((qs[3] + 32, qs[4]), (0, qs[3])):
+    for a, b in ((qs[3] + 64, qs[4]), (0, qs[3])):
         assert (np.abs(got2[a:b] - ref2[a:b]) <= prefill_bound(ref2[a:b], w.dtype)).all()
 
 
