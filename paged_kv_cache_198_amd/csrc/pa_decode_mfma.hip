@@ -70,7 +70,8 @@ struct TileRegs {
 // a suffix item has one member, the sequence itself.  Each column writes a
 // partial to its member's workspace slot, or, for slot -1, the final output.
 template <int DT, int BS, bool GROUP>
-__global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
   constexpr int NC = GROUP ? 16 : kMG;     // columns that produce output
@@ -170,10 +171,21 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   const int wv = __builtin_amdgcn_readfirstlane(w);
   char* vt = smem + w * (kMTile * kVRow);
 
-  // Fused step: the last partition owns position ctx-1.  In the tile that
-  // holds it, the lanes of its row take the new K/V rows of head g from the
-  // inputs instead of the pool and store them into the slot.
+  // Fused step: the last partition owns position ctx-1.  Its new K/V rows of
+  // head g come from the inputs (loaded here with the query; lane (n, q)
+  // holds bytes 16n .. 16n+15), replace that row of the tile in LDS, and are
+  // stored into the slot after the loop.  Without a new token the loads go
+  // through an empty resource and return zeros.
   const bool append = a.new_key != nullptr && ctx > 0 && (GROUP ? owns_last : p == nparts - 1);
+  uint4 nk, nv;
+  {
+    const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * kMD * 2;
+    const uint32_t nbytes = append ? static_cast<uint32_t>(kMD * 2) : 0u;
+    nk = buffer_load16(make_rsrc(append ? static_cast<const char*>(a.new_key) + src : kb, nbytes),
+                       16u * n);
+    nv = buffer_load16(make_rsrc(append ? static_cast<const char*>(a.new_value) + src : vb, nbytes),
+                       16u * n);
+  }
 
   // Issue every load of the tile at t0.  Each block's head tile is one buffer
   // resource; a row past the context, or in a block outside the pool, gets
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
     int blk[NBK];
 #pragma unroll
     for (int b = 0; b < NBK; ++b) {
-      blk[b] = trow[min(t0 / BS + b, last_lb)];
+      blk[b] = table_entry(trow, min(t0 / BS + b, last_lb));
       tl.bok[b] = static_cast<unsigned>(blk[b]) < static_cast<unsigned>(a.NB);
     }
     rsrc_t kres[NBK], vres[NBK];
@@ -213,35 +225,6 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
                          : kOutOfRange;
       tl.vr[j] = buffer_load16(vres[(boff + 4 * j) / BS], voff);
     }
-    if (append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile) {
-      const int rel = ctx - 1 - t0;
-      if (q == rel % 4) {
-        const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * kMD * 2 + 16 * n;
-        const uint4 nk = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_key) + src);
-        const uint4 nv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_value) + src);
-        const int bi = (boff + rel - rel % 4) / BS;   // block of the row group (uniform)
-        int b = blk[0];
-        bool bvalid = tl.bok[0];
-#pragma unroll
-        for (int k = 1; k < NBK; ++k) {
-          b = (k == bi) ? blk[k] : b;
-          bvalid = (k == bi) ? tl.bok[k] : bvalid;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j == rel / 4) {
-            tl.kr[j] = nk;
-            tl.vr[j] = nv;
-          }
-        }
-        if (bvalid) {
-          const size_t dst = static_cast<size_t>(b) * bstride +
-                             static_cast<size_t>((boff + rel) % BS) * (kMD * 2) + 16 * n;
-          *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) = nk;
-          *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
-        }
-      }
-    }
   };
 
   // Scores, online softmax and the V product for the tile at t0 (< end).
@@ -251,6 +234,8 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.kr[j];
+    const bool has_new = append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile;
+    if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nk;
     lds_order();
     f32x4_t sc[2];
 #pragma unroll
@@ -307,6 +292,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
+    if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nv;
     lds_order();
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = mma<DT>(vt_operand(vt, kVRow, dt, n, q), pb, o[dt]);
@@ -314,10 +300,42 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_gqa_mfma_kernel(DecodeArg
   };
 
   constexpr int kStride = kMWaves * kMTile;
-  for (int t0 = start + wv * kMTile; t0 < end; t0 += kStride) {
-    Tile ta;
-    issue(t0, ta);
-    consume(t0, ta);
+  {
+    // Two register stages: the loads of the wavefront's next tile are in
+    // flight while it waits for, and then uses, the current one.
+    // The loads are issued without conditions (a tile past the end loads
+    // zeros without touching memory), so the compiler can count the loads
+    // in flight on every path and wait only for the ones each use needs.
+    Tile ta, tb;
+    const int first = start + wv * kMTile;
+    issue(first, ta);
+    issue(first + kStride, tb);
+    // The query and new-row loads, issued before the tiles', are waited for
+    // here, where the tile loads stay in flight.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    asm volatile("" ::"v"(qt[0]), "v"(qt[1]), "v"(qt[2]), "v"(qt[3]),
+                 "v"(__builtin_bit_cast(u32x4_t, nk)), "v"(__builtin_bit_cast(u32x4_t, nv)));
+    for (int t0 = first; t0 < end; t0 += 2 * kStride) {
+      consume(t0, ta);
+      issue(t0 + 2 * kStride, ta);
+      if (t0 + kStride >= end) break;
+      consume(t0 + kStride, tb);
+      issue(t0 + 3 * kStride, tb);
+    }
+  }
+  // The new token's rows go into its slot after the loop: with no store
+  // before them, the block-table reads above stay scalar loads (a store
+  // through the pool pointers could alias the table as far as the compiler
+  // knows, and a vector load of a table entry would have to wait for every
+  // tile load issued before it).  Only this workgroup reads that slot.
+  if (append && ctx - 1 >= start && ctx - 1 < end && wv == 0 && q == 0) {
+    const int blk = table_entry(trow, (ctx - 1) / BS);
+    if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB)) {
+      const size_t dst = static_cast<size_t>(blk) * bstride +
+                         static_cast<size_t>((ctx - 1) % BS) * (kMD * 2) + 16 * n;
+      *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) = nk;
+      *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
+    }
   }
   __syncthreads();                         // every wavefront is done with its tile
 

@@ -108,6 +108,16 @@ __device__ __forceinline__ float row_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A block-table entry at a wavefront-uniform index, read through the
+// constant address space: the table is never written during a launch, and
+// loads from that space at uniform addresses become scalar loads even after
+// stores or memory barriers in the kernel (a vector load of the entry would
+// wait on the vector-memory counter, i.e. for every K/V load issued before it).
+__device__ __forceinline__ int32_t table_entry(const int32_t* row, int i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(row))[i];
+}
+
 struct DecodeArgs {
   void* out;
   const void* q;
