@@ -121,15 +121,16 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const int wend = __builtin_amdgcn_readfirstlane(wlast);
 
   // B operand of S^T = K Q^T: lane (n, q4) holds q[column n][32kk + 8q4 .. +8]
+  // (loaded without a branch from a row that always exists, nq >= 1 here;
+  // columns without a query then take zeros)
   u16x8_t qt[4];
   {
     const T* qb = static_cast<const T*>(a.q) +
-                  (static_cast<size_t>(r0 + min(qi, max(nq - 1, 0))) * a.Hq + h) * kPD;
+                  (static_cast<size_t>(r0 + min(qi, nq - 1)) * a.Hq + h) * kPD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col_valid) v = *reinterpret_cast<const uint4*>(qb + 32 * kk + 8 * q4);
-      qt[kk] = as_u16x8(v);
+      const uint4 v = *reinterpret_cast<const uint4*>(qb + 32 * kk + 8 * q4);
+      qt[kk] = as_u16x8(col_valid ? v : make_uint4(0, 0, 0, 0));
     }
   }
 
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   };
   auto issue = [&](int t0, Stage& st) {
     const int lb = min(t0 + kPRowsW * wv, max(kend - 1, 0)) / BS;   // wave-uniform
-    const int blk = trow[lb];
+    const int blk = table_entry(trow, lb);
     const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
     const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
     const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
@@ -284,16 +285,22 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<uint4*>(vs + r * kPRowV + 16 * lcol) = st.vr[j];
     }
     __syncthreads();
-    if (t0 + 2 * kPTile < kend) issue(t0 + 2 * kPTile, st);
+    issue(t0 + 2 * kPTile, st);            // past kend: zero loads, no traffic
     if (t0 <= wend) compute(t0);
   };
 
+  // The stages are issued without conditions, so the compiler counts the
+  // loads in flight exactly on every path and each wait leaves the other
+  // stage's loads outstanding; the query loads (older) are waited for here.
   Stage sa, sb;
-  if (kend > 0) issue(0, sa);
-  if (kPTile < kend) issue(kPTile, sb);
+  issue(0, sa);
+  issue(kPTile, sb);
+  asm volatile("" ::"v"(qt[0]), "v"(qt[1]), "v"(qt[2]), "v"(qt[3]));
+  // Whole pairs of steps, without a break between them: a second step past
+  // kend stages zeros and skips its products (t0 > wend), and the loop's
+  // single exit keeps the load counts the same on every path.
   for (int t0 = 0; t0 < kend; t0 += 2 * kPTile) {
     step(t0, sa);
-    if (t0 + kPTile >= kend) break;
     step(t0 + kPTile, sb);
   }
 
