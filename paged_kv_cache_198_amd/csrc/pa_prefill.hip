@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   // zero probability and leave the running max alone)
   const int wlast = qbase + w * TPW < nq ? ctx - nq + min(qbase + w * TPW + TPW, nq) - 1 : -1;
   const int wend = __builtin_amdgcn_readfirstlane(wlast);
+  // the first position of the wavefront's columns when all of them hold a
+  // query (else -1: every tile takes the mask)
+  const int wfirst = __builtin_amdgcn_readfirstlane(
+      qbase + w * TPW + TPW <= nq ? ctx - nq + qbase + w * TPW : -1);
 
   // B operand of S^T = K Q^T: lane (n, q4) holds q[column n][32kk + 8q4 .. +8]
   // (loaded without a branch from a row that always exists, nq >= 1 here;
@@ -192,19 +196,31 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
         }
       }
       // Causal mask; rows of blocks outside the pool were loaded as zeros
-      // and count as zero keys and values.
+      // and count as zero keys and values.  A tile that ends before the
+      // wavefront's first position (all its columns valid) needs no mask.
       float sv[8];
       float mt = kNegInf;
-      const int lim = col_valid ? pos - t0 : -1;   // rows r <= lim take part
+      if (t0 + kPTile - 1 <= wfirst) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * u + 4 * q4 + i;
-          const float x = r <= lim ? sc[u][i] * a.qscale : kNegInf;
-          sv[4 * u + i] = x;
-          mt = fmaxf(mt, x);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float x = sc[u][i] * a.qscale;
+            sv[4 * u + i] = x;
+            mt = fmaxf(mt, x);
+          }
+      } else {
+        const int lim = col_valid ? pos - t0 : -1;   // rows r <= lim take part
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * u + 4 * q4 + i;
+            const float x = r <= lim ? sc[u][i] * a.qscale : kNegInf;
+            sv[4 * u + i] = x;
+            mt = fmaxf(mt, x);
+          }
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const bool bump = mt > m_run + kPLazy;
