@@ -130,7 +130,8 @@ struct DecodeArgs {
   float* ws_o;
   // Fused step (pa_decode_step): the token at position ctx-1 of each
   // sequence, [S][Hkv][D]; null for plain attention.  The workgroup that
-  // owns that position writes it into its slot and uses it from registers.
+  // owns that position writes it into its slot and uses it without reading
+  // the pool.
   const void* new_key;
   const void* new_value;
   // Prefix sharing (pa_decode_cascade), null otherwise: sequence s's own
