@@ -494,6 +494,20 @@ BEAM_BENCH = dict(requests=16, width=4, layers=40, Hq=40, Hkv=40, D=128, dtype="
                   NB=4096, prompt=(384, 640))
 
 
+class _HostBeams:
+    """The allocator side of a beam run without pools: the same creates,
+    forks, frees and appends (engine.beam_reselect only forks and frees)."""
+
+    def __init__(self, pa, num_blocks, bs):
+        self.alloc = pa.Allocator(num_blocks, bs)
+
+    def fork(self, parent, child):
+        self.alloc.fork(parent, child)
+
+    def free(self, seq_id):
+        self.alloc.free(seq_id)
+
+
 def run_beam(args, pa, synth, torch):
     """Beam search on a 40-layer, LLaMA-13B-shaped attention stack: 16
     requests x 4 beams whose prompts are shared by their beams.  One step =
@@ -505,6 +519,9 @@ def run_beam(args, pa, synth, torch):
     import time
     from paged_kv_cache_198_amd import engine
     c = dict(BEAM_BENCH)
+    # --bs picks the block size; the pool keeps the same token capacity
+    c["NB"] = c["NB"] * c["bs"] // args.bs
+    c["bs"] = args.bs
     R, W, L, bs = c["requests"], c["width"], c["layers"], c["bs"]
     dt = synth.KV_DTYPES[c["dtype"]]
     gen = torch.Generator(device="cuda")
@@ -566,13 +583,30 @@ def run_beam(args, pa, synth, torch):
         stop.record()
         torch.cuda.synchronize()
         ms = start.elapsed_time(stop) / args.steps
-        return ms, {k: v / args.steps for k, v in stats.items()}, kv
+        return ms, {k: v / args.steps for k, v in stats.items()}, kv, beams
 
-    plain_ms, plain_st, kv = run(False)
+    plain_ms, plain_st, kv, _ = run(False)
     used_plain = kv.used_blocks()
     del kv
     torch.cuda.empty_cache()
-    ms, st, kv = run(True)
+    ms, st, kv, end_beams = run(True)
+    held = kv.used_blocks() * bs
+    host = _HostBeams(pa, c["NB"] * bs, 1)
+    hbeams, hnext = [], R
+    for r in range(R):
+        host.alloc.create(r)
+        host.alloc.append_n(r, int(plens[r]))
+        group = [r]
+        for _ in range(W - 1):
+            host.fork(r, hnext)
+            group.append(hnext)
+            hnext += 1
+        hbeams.append(group)
+    for t in range(total):
+        hbeams, hnext = engine.beam_reselect(host, hbeams, choices[t], hnext)
+        for b in (b for g in hbeams for b in g):
+            host.alloc.append(b)
+    tree = c["NB"] * bs - host.alloc.num_free()
     gbs = lambda b, m: b / (m * 1e-3) / 1e9
     return {
         "metric": "beam-search decode step over 40 layers: KV GB/s (logical) + us/step",
@@ -591,11 +625,19 @@ def run_beam(args, pa, synth, torch):
                      "kernel": "whole beam step (copies + 40 x (item kernel + reduce))",
                      "note": "achieved counts the K/V bytes the cascade must read per step"},
         "per_step": {"cow_copies": st["copies"], "logical_kv_bytes": st["logical"],
-                     "read_kv_bytes": st["read"], "host_us": st["host_s"] * 1e6},
+                     "read_kv_bytes": st["read"], "host_us": st["host_s"] * 1e6,
+                     # each copy moves a whole block of K and V in every layer
+                     "cow_bytes_moved": st["copies"] * 2 * L * bs * c["Hkv"] * c["D"] * eb * 2},
         "plain_fused_step": {"us": plain_ms * 1e3, "logical_GBs": gbs(plain_st["logical"], plain_ms),
                              "host_us": plain_st["host_s"] * 1e6,
                              "speedup_of_cascade": plain_ms / ms},
         "blocks_used_per_layer": {"plain_run_end": used_plain, "cascade_run_end": kv.used_blocks()},
+        "slots_per_layer_at_end": {
+            "held": held, "beam_tree_tokens": tree,
+            "waste": 1 - tree / held,
+            "note": "slots held in one layer's pool after the run against the distinct "
+                    "tokens of the beam tree (the same run on one-token blocks, which "
+                    "have no tails and never copy)"},
         "cpu_baseline": None,
     }
 
@@ -644,9 +686,13 @@ def main():
             s_ms, _ = other.run(max(20, args.steps // 4), args.warmup, fused=True)
             lens_h = other.lens.cpu().numpy().astype(np.int64)
             blocks = (lens_h + bs - 1) // bs
+            # closed form: with residues spread evenly, a sequence's last
+            # block leaves (bs - 1) / 2 slots empty on average
+            mod_w = len(lens_h) * (bs - 1) / 2
             sweep[f"bs{bs}"] = {"us_per_step": s_ms * 1e3,
                                 "tail_waste": float((blocks * bs - lens_h).sum()
                                                     / (blocks * bs).sum()),
+                                "tail_waste_model": float(mod_w / (lens_h.sum() + mod_w)),
                                 "GBs": other.kv_bytes / (s_ms * 1e-3) / 1e9,
                                 "frac_hbm_peak": other.kv_bytes / (s_ms * 1e-3) / 1e9
                                 / HBM_PEAK_GBS}

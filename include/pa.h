@@ -285,13 +285,14 @@ int pa_decode_cascade(void* out, const void* query, const void* key, const void*
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostic, not part of the path: reads `bytes` (a multiple of 16) of
- * device memory at `src` with the decode kernels' 16-byte non-temporal loads
- * in a grid-stride loop, so a timed call measures the read rate a plain
- * streaming kernel reaches on this GPU (the practical ceiling the decode
- * kernels' fraction of the nominal peak is read against).  Each thread
- * stores one folded word into out (device, out_words >= 256; the launch uses
- * min(out_words / 256, 4096) workgroups of 256 threads).  Asynchronous on
- * `stream`. */
+ * device memory at `src` with the decode kernels' 16-byte non-temporal loads,
+ * in contiguous 32 KB slices (workgroup b takes slices b, b + grid, ...; in a
+ * slice, thread t reads chunks 256 u + t, u = 0..7), so a timed call
+ * measures the read rate a plain streaming kernel reaches on this GPU (the
+ * practical ceiling the decode kernels' fraction of the nominal peak is read
+ * against).  Each thread stores the XOR of the words it read into out
+ * (device, out_words >= 256; the launch uses min(out_words / 256, 4096)
+ * workgroups of 256 threads).  Asynchronous on `stream`. */
 int pa_probe_read_bandwidth(const void* src, size_t bytes, uint32_t* out, int32_t out_words,
                             void* stream);
 

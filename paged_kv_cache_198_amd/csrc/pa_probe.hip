@@ -16,17 +16,28 @@ namespace {
 
 constexpr int kProbeThreads = 256;
 
-// Grid-stride read of n16 16-byte chunks; every thread folds what it read
+// Read of n16 16-byte chunks in contiguous 32 KB slices, workgroups
+// striding over the slices: within a slice each wavefront instruction reads
+// 1 KB of consecutive bytes and eight are in flight per thread, the access
+// shape of the decode kernels' row loads.  Every thread folds what it read
 // into one word and stores it (a plain vector store per thread), so the
 // loads cannot be dropped.
 __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4_t* src,
                                                                    size_t n16, uint32_t* out) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * kProbeThreads;
-  size_t i = static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
+  constexpr int kUnroll = 8;
+  constexpr size_t kSlice = static_cast<size_t>(kProbeThreads) * kUnroll;   // chunks
+  const int tid = threadIdx.x;
   uint32_t acc = 0;
-  for (; i < n16; i += stride) {
-    const u32x4_t v = __builtin_nontemporal_load(src + i);
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  for (size_t base = static_cast<size_t>(blockIdx.x) * kSlice; base < n16;
+       base += static_cast<size_t>(gridDim.x) * kSlice) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + static_cast<size_t>(u) * kProbeThreads + tid;
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = acc;
 }

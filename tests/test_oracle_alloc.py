@@ -126,6 +126,25 @@ def pin_tail_only_waste():
         assert len(set(blocks)) == len(blocks)
 
 
+def pin_tail_waste_closed_form():
+    """The block-size cost model's waste term: blocks are acquired as a
+    sequence grows, so only its last block has empty slots, bs - (n mod bs)
+    of them unless n fills it.  Over one sequence per residue class the
+    empty slots add up to exactly bs (bs - 1) / 2, i.e. (bs - 1) / 2 per
+    sequence, the model's expected tail waste."""
+    rng = np.random.default_rng(7)
+    for bs in (8, 16, 32):
+        a = Allocator(4096, bs)
+        empty = 0
+        for r in range(bs):
+            n = bs * int(rng.integers(1, 4)) + r
+            a.create(r)
+            for _ in range(n):
+                a.append(r)
+            empty += len(a.tables[r]) * bs - n
+        assert 2 * empty == bs * (bs - 1)
+
+
 def pin_lazy_cow_count():
     """n sequences sharing a half-filled block: the first n-1 writers copy,
     the last one writes in place; a full shared block is never copied."""
@@ -271,7 +290,7 @@ def pin_system_prompt_saving():
     assert private - used == len(own) * 64
 
 
-PINS = [pin_trace, pin_random_ops, pin_tail_only_waste, pin_lazy_cow_count, pin_sharing_saving,
+PINS = [pin_trace, pin_random_ops, pin_tail_only_waste, pin_tail_waste_closed_form, pin_lazy_cow_count, pin_sharing_saving,
         pin_prefix_trace, pin_prefix_random_ops, pin_system_prompt_saving]
 
 
