@@ -13,10 +13,10 @@
 // ordered so each XCD runs whole (s, g) pairs (see the kernel's prologue).  A
 // wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
 // KV head g, each column with its own causal limit.  Per 32-token key tile:
-//   * all 512 lanes load the tile's K and V rows once (16 bytes each, raw
+//   * all 512 lanes load 64 keys' K and V rows once (16 bytes each, raw
 //     buffer loads that return zero past a block or the range) into LDS,
-//     where the eight wavefronts share them; the next tiles' loads are
-//     issued before the current tile is used;
+//     where the eight wavefronts share them as two 32-key tiles; the next
+//     64 keys' loads are issued before the current ones are used;
 //   * S^T = K . Q^T (2 x 4 v_mfma_f32_16x16x32): A = K rows from LDS, B = the
 //     wavefront's queries in registers; lane l then holds 8 scores of
 //     column l%16;
@@ -43,8 +43,9 @@ namespace {
 using namespace mfma;
 
 constexpr int kPWaves = 8;                 // wavefronts per workgroup
-constexpr int kPRowsW = 32 / kPWaves;      // tile rows each wavefront loads
-constexpr int kPTile = 32;                 // keys per tile
+constexpr int kPTile = 32;                 // keys per product tile
+constexpr int kPStage = 64;                // keys staged in LDS per barrier pair
+constexpr int kPRowsW = kPStage / kPWaves; // staged rows each wavefront loads
 constexpr int kPD = 128;                   // head dim
 // Padded LDS rows.  K rows (68 dwords) let the 16 lanes of an operand read
 // (rows n = 0..15, 16 bytes each) hit 16 distinct bank groups; V rows (72
@@ -77,8 +78,8 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int QT = kPWaves * TPW;        // query tokens per workgroup
   static_assert(BS >= 8 && (BS % 8 == 0), "block size");
 
-  __shared__ __attribute__((aligned(16))) char ks[kPTile * kPRow];
-  __shared__ __attribute__((aligned(16))) char vs[kPTile * kPRowV];
+  __shared__ __attribute__((aligned(16))) char ks[kPStage * kPRow];
+  __shared__ __attribute__((aligned(16))) char vs[kPStage * kPRowV];
 
   // XCD-aware order.  The hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kPD * 2;
   const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kPD * 2;
 
-  // Cooperative tile load: wavefront w carries rows 4w .. 4w+3 (lane l: row
-  // 4w + l/16, 16-byte column l%16).  The four rows sit in one block (bs >= 8,
-  // tiles start at multiples of 32), so one table entry and one buffer
-  // resource per pool serve the wavefront.  Two register stages alternate,
-  // so a tile's loads are issued two tiles before it is used.
+  // Cooperative stage load: wavefront w carries staged rows 8w .. 8w+7 (lane
+  // l: rows 8w + l/16 and 8w + 4 + l/16, 16-byte column l%16).  The eight
+  // rows sit in one block (bs >= 8, stages start at multiples of 64), so one
+  // table entry and one buffer resource per pool serve the wavefront.  The
+  // next stage's loads are issued as soon as the current one is in LDS.
   const int wv = __builtin_amdgcn_readfirstlane(w);
   constexpr int NJ = kPRowsW / 4;          // 16-lane row groups per wavefront
   const int lrow = kPRowsW * wv + (lane >> 4);
@@ -171,10 +172,10 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     const rsrc_t vres = make_rsrc(vb + off, bytes);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      // row within its block: t0 is a multiple of 32, so for bs <= 32 it is
-      // the lane's tile row mod bs, else the tile's offset plus that row
+      // row within its block: t0 is a multiple of 64, so for bs <= 64 it is
+      // the lane's staged row mod bs, else the stage's offset plus that row
       const uint32_t r = static_cast<uint32_t>(lrow + 4 * j);
-      const uint32_t rib = BS > kPTile ? (static_cast<uint32_t>(t0) & (BS - 1)) + r : r & (BS - 1);
+      const uint32_t rib = BS > kPStage ? (static_cast<uint32_t>(t0) & (BS - 1)) + r : r & (BS - 1);
       const uint32_t in = rib * (kPD * 2) + 16u * static_cast<uint32_t>(lcol);
       const uint32_t voff = t0 + static_cast<int>(r) < kend ? in : kOutOfRange;
       st.kr[j] = buffer_load16(kres, voff);
@@ -182,7 +183,8 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  auto compute = [&](int t0) {
+  // products of the 32-key tile at t0, staged at LDS row rb
+  auto compute = [&](int t0, int rb) {
       // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
       f32x4_t sc[2];
 #pragma unroll
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const uint4 ka =
-              *reinterpret_cast<const uint4*>(ks + (16 * u + n) * kPRow + 64 * kk + 16 * q4);
+              *reinterpret_cast<const uint4*>(ks + (rb + 16 * u + n) * kPRow + 64 * kk + 16 * q4);
           sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
         }
       }
@@ -284,16 +286,18 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       // read 16 rows down gives the other four.
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u16x8_t va = vt_operand(vs, kPRowV, dt, n, q4);
+        const u16x8_t va = vt_operand(vs + rb * kPRowV, kPRowV, dt, n, q4);
         o[dt] = mma<DT>(va, pb, o[dt]);
         if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
       }
   };
 
-  // one tile: publish stage `st` in LDS, refill it with the tile two ahead,
-  // then use the published tile
-  auto step = [&](int t0, Stage& st) {
-    __syncthreads();                       // every wavefront is done with the last tile
+  // one stage: publish the 64 staged keys in LDS, refill the registers with
+  // the next 64 (past kend: zero loads, no traffic), then the two 32-key
+  // product tiles (skipped past the wavefront's last position)
+  Stage st;
+  auto step = [&](int t0) {
+    __syncthreads();                       // every wavefront is done with the last stage
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int r = lrow + 4 * j;
@@ -301,24 +305,16 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<uint4*>(vs + r * kPRowV + 16 * lcol) = st.vr[j];
     }
     __syncthreads();
-    issue(t0 + 2 * kPTile, st);            // past kend: zero loads, no traffic
-    if (t0 <= wend) compute(t0);
+    issue(t0 + kPStage, st);
+    if (t0 <= wend) compute(t0, 0);
+    if (t0 + kPTile <= wend) compute(t0 + kPTile, kPTile);
   };
 
-  // The stages are issued without conditions, so the compiler counts the
-  // loads in flight exactly on every path and each wait leaves the other
-  // stage's loads outstanding; the query loads (older) are waited for here.
-  Stage sa, sb;
-  issue(0, sa);
-  issue(kPTile, sb);
+  // The query loads (older than the stage's) are waited for before the loop,
+  // where the stage's loads stay in flight.
+  issue(0, st);
   asm volatile("" ::"v"(qt[0]), "v"(qt[1]), "v"(qt[2]), "v"(qt[3]));
-  // Whole pairs of steps, without a break between them: a second step past
-  // kend stages zeros and skips its products (t0 > wend), and the loop's
-  // single exit keeps the load counts the same on every path.
-  for (int t0 = 0; t0 < kend; t0 += 2 * kPTile) {
-    step(t0, sa);
-    step(t0 + kPTile, sb);
-  }
+  for (int t0 = 0; t0 < kend; t0 += kPStage) step(t0);
 
   // column n's sum over the four lane groups, then this lane's four dims of
   // each 16-dim slice
