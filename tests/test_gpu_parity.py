@@ -964,6 +964,11 @@ PREFILL_CASES = [  # (G, Hkv, bs, dtype, prefix law, chunk law)
     (8, 2, 64, "bf16", ("uniform", 0, 700), ("uniform", 1, 90)),
     (8, 4, 128, "bf16", ("fixed", 0), ("fixed", [1, 2, 31, 32, 33, 64])),
     (1, 2, 128, "f16", ("fixed", [0, 127, 128, 129, 5, 1000]), ("fixed", [0, 1, 64, 65, 300, 7])),
+    # query tiles of 64 rows (G = 2) cut just before, at and after their end;
+    # key ranges ending off the 64-key stages
+    (2, 3, 16, "bf16", ("fixed", [0, 63, 64, 65, 1, 190]), ("fixed", [63, 64, 65, 127, 128, 129])),
+    (4, 2, 128, "f16", ("fixed", [33, 0, 191, 64, 250, 3]), ("fixed", [31, 32, 33, 96, 5, 200])),
+    (1, 1, 8, "bf16", ("fixed", [7, 8, 9, 56, 57, 500]), ("fixed", [121, 8, 199, 1, 72, 13])),
 ]
 
 
