@@ -15,6 +15,8 @@
 //   * K and V rows are loaded coalesced (16 lanes x 16 B per 256-byte row)
 //     with raw buffer loads, one resource per block; rows past the context
 //     load zero without touching memory, so no load sits behind a branch.
+//     Two register stages keep the wavefront's next tile in flight while
+//     it uses the current one.
 //   * S^T = K . Q^T, as two 16-token MFMA tiles x 4 k-steps of 32 dims:
 //     A = K through the wavefront's LDS tile (lane l: token l%16, dims
 //     8*(l/16) + 32kk .. +8, one 16-byte read), B = Q^T kept in registers
@@ -27,9 +29,9 @@
 //   * O^T += V^T . P^T: B = P^T is already where the scores left it (lane l:
 //     head l%16, the 8 tokens 4(l/16)+i and 16+4(l/16)+i), A = V^T comes from
 //     the same LDS tile, now holding the V rows (rows padded to 272 bytes),
-//     through the transposing LDS read (two 8-byte reads per 16 dims).  The output rows of O^T are dims
-//     and its columns heads, so lane l holds head l%16: the per-head rescale
-//     factor never leaves the lane.
+//     through the transposing LDS read (two 8-byte reads per 16 dims).  The
+//     output rows of O^T are dims and its columns heads, so lane l holds head
+//     l%16: the per-head rescale factor never leaves the lane.
 // Probabilities enter the second product rounded to the KV type; the running
 // sum adds the same rounded values, so numerator and denominator agree.
 #include <hip/hip_runtime.h>
