@@ -10,28 +10,32 @@
 // the step stays bound by HBM, the matrix cores only take the arithmetic off
 // the vector ALUs.
 //
-// Per wavefront and 32-token tile (t0 a multiple of 32, so the tile starts on
-// a block boundary for bs in {8, 16, 32}):
+// Per wavefront and 16-token tile (t0 a multiple of 16, so the tile starts on
+// a block boundary for bs in {8, 16}, and sits inside one block for larger
+// bs):
 //   * K and V rows are loaded coalesced (16 lanes x 16 B per 256-byte row)
 //     with raw buffer loads, one resource per block; rows past the context
 //     load zero without touching memory, so no load sits behind a branch.
 //     Two register stages keep the wavefront's next tile in flight while
-//     it uses the current one.
-//   * S^T = K . Q^T, as two 16-token MFMA tiles x 4 k-steps of 32 dims:
-//     A = K through the wavefront's LDS tile (lane l: token l%16, dims
-//     8*(l/16) + 32kk .. +8, one 16-byte read), B = Q^T kept in registers
-//     (lane l: head l%16, zero for the padding heads).  Lane l then holds the
-//     scores of tokens 16u + 4(l/16) + i (i = 0..3) for head l%16.
+//     it uses the current one.  Small tiles keep the registers at about 150,
+//     three wavefronts per SIMD, and spread short ranges over all four
+//     wavefronts of a workgroup.
+//   * S^T = K . Q^T, one 16-token MFMA tile x 4 k-steps of 32 dims
+//     (v_mfma_f32_16x16x32): A = K through the wavefront's LDS tile (lane l:
+//     token l%16, dims 8*(l/16) + 32kk .. +8, one 16-byte read), B = Q^T kept
+//     in registers (lane l: head l%16, zero for the padding heads).  Lane l
+//     then holds the scores of tokens 4(l/16) + i (i = 0..3) for head l%16.
 //   * online softmax per head (max across the 4 lane groups of a head with
 //     two shuffles; the running sum stays per lane and is added up at the
 //     end); the reference max moves only when it grows by more than 2^8, so
 //     the accumulators are rarely rescaled.
-//   * O^T += V^T . P^T: B = P^T is already where the scores left it (lane l:
-//     head l%16, the 8 tokens 4(l/16)+i and 16+4(l/16)+i), A = V^T comes from
-//     the same LDS tile, now holding the V rows (rows padded to 272 bytes),
-//     through the transposing LDS read (two 8-byte reads per 16 dims).  The
-//     output rows of O^T are dims and its columns heads, so lane l holds head
-//     l%16: the per-head rescale factor never leaves the lane.
+//   * O^T += V^T . P^T on v_mfma_f32_16x16x16 (K = the tile's 16 tokens):
+//     B = P^T is already where the scores left it (lane l: head l%16, tokens
+//     4(l/16) + i), A = V^T comes from the same LDS tile, now holding the V
+//     rows (rows padded to 272 bytes), through one transposing LDS read
+//     (ds_read_b64_tr_b16) per 16 dims.  The output rows of O^T are dims and
+//     its columns heads, so lane l holds head l%16: the per-head rescale
+//     factor never leaves the lane.
 // Probabilities enter the second product rounded to the KV type; the running
 // sum adds the same rounded values, so numerator and denominator agree.
 #include <hip/hip_runtime.h>
@@ -46,7 +50,7 @@ namespace pa {
 namespace {
 
 constexpr int kMWaves = 4;                 // wavefronts per workgroup
-constexpr int kMTile = 32;                 // tokens per wavefront per tile
+constexpr int kMTile = 16;                 // tokens per wavefront per tile
 constexpr int kMD = 128;                   // head dim
 constexpr int kMG = 8;                     // query heads per KV head
 constexpr int kVRow = kMD * 2 + 16;        // padded LDS row of one V token (bytes)
@@ -57,10 +61,11 @@ constexpr float kLazy = 8.f;               // lazy-rescale threshold (log2 units
 
 // Registers of one tile in flight: K and V rows (token t0 + 4j + q, 16-byte
 // column n), block flags.
+constexpr int kMRowGroups = kMTile / 4;    // 4-row load groups per tile
 template <int NBK>
 struct TileRegs {
-  uint4 kr[8];
-  uint4 vr[8];
+  uint4 kr[kMRowGroups];
+  uint4 vr[kMRowGroups];
   bool bok[NBK];
 };
 
@@ -72,7 +77,7 @@ struct TileRegs {
 // a suffix item has one member, the sequence itself.  Each column writes a
 // partial to its member's workspace slot, or, for slot -1, the final output.
 template <int DT, int BS, bool GROUP>
-__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
@@ -212,36 +217,37 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
     // K and V rows, coalesced: 16 lanes x 16 B per 256-byte row, four rows
     // (tokens t0 + 4j + q) per instruction.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kMRowGroups; ++j) {
       const int rel = 4 * j + q;
       const uint32_t voff =
           t0 + rel < end ? static_cast<uint32_t>(((boff + rel) % BS) * (kMD * 2) + 16 * n)
                          : kOutOfRange;
-      tl.kr[j] = buffer_load16(kres[(boff + 4 * j) / BS], voff);
+      tl.kr[j] = buffer_load16(kres[NBK == 1 ? 0 : (boff + 4 * j) / BS], voff);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kMRowGroups; ++j) {
       const int rel = 4 * j + q;
       const uint32_t voff =
           t0 + rel < end ? static_cast<uint32_t>(((boff + rel) % BS) * (kMD * 2) + 16 * n)
                          : kOutOfRange;
-      tl.vr[j] = buffer_load16(vres[(boff + 4 * j) / BS], voff);
+      tl.vr[j] = buffer_load16(vres[NBK == 1 ? 0 : (boff + 4 * j) / BS], voff);
     }
   };
 
   // Scores, online softmax and the V product for the tile at t0 (< end).
+  constexpr int NU = kMTile / 16;          // 16-token score sub-tiles
   auto consume = [&](int t0, const Tile& tl) {
     // K rows through LDS into the A-operand layout: lane (n, q) of sub-tile
     // u takes 16 bytes of token 16u + n at dims 32kk + 8q.
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kMRowGroups; ++j)
       *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.kr[j];
     const bool has_new = append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile;
     if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nk;
     lds_order();
-    f32x4_t sc[2];
+    f32x4_t sc[NU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -251,10 +257,10 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       }
     }
     lds_order();
-    float sv[8];
+    float sv[4 * NU];
     float mt = kNegInf;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rel = 16 * u + 4 * q + i;
@@ -278,13 +284,13 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
     }
     m_run = mn;
-    u16x8_t pb;
+    uint16_t pbits[4 * NU];
     float psum = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = 0; jj < 4 * NU; ++jj) {
       const float pv = (sv[jj] == kNegInf) ? 0.f : fast_exp2(sv[jj] - mn);
       const uint16_t bits = to_bits<DT>(pv);
-      pb[jj] = bits;
+      pbits[jj] = bits;
       psum += from_bits<DT>(bits);
     }
     l_run += psum;
@@ -292,12 +298,25 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
     // V rows to LDS (over the K rows, whose reads are done), then read back
     // transposed.
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kMRowGroups; ++j)
       *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
     if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nv;
     lds_order();
+    if constexpr (NU == 2) {
+      u16x8_t pb;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = mma<DT>(vt_operand(vt, kVRow, dt, n, q), pb, o[dt]);
+      for (int jj = 0; jj < 8; ++jj) pb[jj] = pbits[jj];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] = mma<DT>(vt_operand(vt, kVRow, dt, n, q), pb, o[dt]);
+    } else {
+      // 16 tokens: the 16x16x16 product, B = this lane's 4 probabilities
+      u16x4_t pb;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) pb[jj] = pbits[jj];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = mma16<DT>(vt_operand16(vt, kVRow, dt, n, q), pb, o[dt]);
+    }
     lds_order();                           // the next tile rewrites these rows
   };
 

@@ -164,8 +164,9 @@ struct PartRange {
   int start, end, slot, nparts, total;
 };
 
-// `align` (a multiple of 32 and of bs) rounds seq_start down, so tiles and
-// row groups always start on the boundaries the kernels assume.
+// `align` (a multiple of the caller's tile and of bs) rounds seq_start
+// down, so tiles and row groups always start on the boundaries the kernels
+// assume.
 __device__ __forceinline__ PartRange part_range(const DecodeArgs& a, int s, int p, int ctx,
                                                 int align) {
   const int s0 = a.seq_start ? min(max(a.seq_start[s], 0) / align * align, ctx) : 0;

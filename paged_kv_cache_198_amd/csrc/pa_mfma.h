@@ -1,6 +1,7 @@
 // Matrix-core helpers shared by the decode and prefill kernels (gfx950):
-// the 16x16x32 bf16/f16 MFMA, 16-bit KV bit patterns, raw buffer loads that
-// return zero past a resource's end, and same-wavefront LDS ordering.
+// the 16x16x32 and 16x16x16 bf16/f16 MFMA, 16-bit KV bit patterns, raw
+// buffer loads that return zero past a resource's end, and same-wavefront
+// LDS ordering.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +25,21 @@ __device__ __forceinline__ f32x4_t mma(const u16x8_t& a, const u16x8_t& b, const
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// The 16x16x16 product (K = 16): A and B carry 4 16-bit values per lane.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mma16(const u16x4_t& a, const u16x4_t& b, const f32x4_t& c) {
+  if constexpr (DT == PA_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
 }
 
 // float -> 16-bit pattern of the KV type (round to nearest even) and back.
@@ -100,6 +116,14 @@ __device__ __forceinline__ u16x8_t vt_operand(const char* tile, int stride, int 
   const v4s_t lo = ds_read_tr16(p0);
   const v4s_t hi = ds_read_tr16(p0 + 16 * stride);
   return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand of O^T += V^T P^T for a 16-row tile (the 16x16x16 product):
+// lane (n, q) gets dims 16dt + n of rows 4q .. 4q+3.
+__device__ __forceinline__ u16x4_t vt_operand16(const char* tile, int stride, int dt, int n,
+                                                int q) {
+  const char* p0 = tile + (4 * q + (n >> 2)) * stride + (16 * dt + 4 * (n & 3)) * 2;
+  return __builtin_bit_cast(u16x4_t, ds_read_tr16(p0));
 }
 
 }  // namespace mfma

@@ -581,7 +581,7 @@ def test_engine_shared_prefix(prompt_len):
 
 
 # ---------------------------------------------------------------------------
-# block sizes 64 and 128 (a 32-token MFMA tile then sits inside one block)
+# block sizes 64 and 128 (a 16-token MFMA tile then sits inside one block)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("bs", [64, 128])
 def test_large_blocks_mha(bs):
