@@ -17,9 +17,9 @@
 //     with raw buffer loads, one resource per block; rows past the context
 //     load zero without touching memory, so no load sits behind a branch.
 //     Two register stages keep the wavefront's next tile in flight while
-//     it uses the current one.  Small tiles keep the registers at about 150,
-//     three wavefronts per SIMD, and spread short ranges over all four
-//     wavefronts of a workgroup.
+//     it uses the current one.  Small tiles keep the registers at about 150
+//     (three wavefronts per SIMD); workgroups of two wavefronts keep short
+//     ranges from leaving wavefronts idle.
 //   * S^T = K . Q^T, one 16-token MFMA tile x 4 k-steps of 32 dims
 //     (v_mfma_f32_16x16x32): A = K through the wavefront's LDS tile (lane l:
 //     token l%16, dims 8*(l/16) + 32kk .. +8, one 16-byte read), B = Q^T kept
@@ -49,7 +49,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kMWaves = 4;                 // wavefronts per workgroup
+constexpr int kMWaves = 2;                 // wavefronts per workgroup
 constexpr int kMTile = 16;                 // tokens per wavefront per tile
 constexpr int kMD = 128;                   // head dim
 constexpr int kMG = 8;                     // query heads per KV head
