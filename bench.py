@@ -77,7 +77,8 @@ def parse():
 def default_partition(workload: str) -> int:
     """Partition size per workload: the long-context batch has only S*Hkv = 64
     (sequence, KV head) pairs, so it is split into 512-token partitions to
-    fill the chip; the others run in one pass."""
+    fill the chip; the 7B batch's short lognormal contexts are split at 512
+    tokens too, which evens out its workgroups; the others run in one pass."""
     from paged_kv_cache_198_amd import synth
     return synth.CONFIGS[workload]["partition_tokens"]
 
@@ -148,8 +149,9 @@ def kernel_name(st) -> str:
     mfma = (w.dtype in ("bf16", "f16") and w.D == 128 and w.Hq // w.Hkv == 8
             and st.part % 32 == 0)
     k = "pa::decode_gqa_mfma_kernel" if mfma else "pa::decode_kernel"
-    return k + (" + reduce_kernel" if st.part and st.max_ctx > st.part else "") + \
-        " (pa_decode_step, fused cache write)"
+    parts = -(-st.max_ctx // st.part) if st.part else 1
+    red = "" if parts < 2 else (" + reduce_wide_kernel" if parts >= 16 else " + reduce_kernel")
+    return k + red + " (pa_decode_step, fused cache write)"
 
 
 def describe(name, w) -> str:

@@ -47,6 +47,7 @@ namespace pa {
 
 constexpr int kWaves = PA_DECODE_WAVES;   // wavefronts per workgroup
 constexpr int kRows = PA_DECODE_ROWS;     // token rows per lane per tile (G < 4)
+constexpr int kWideReduceParts = 16;      // reduce_wide_kernel from this many partitions on
 
 template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
@@ -330,6 +331,83 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
       narrow<DT>(dn > 0.f ? nt / dn : 0.f);
 }
 
+// The same combination for many partitions (long contexts).  One workgroup
+// of 256 threads per (query head, sequence): a partition's row of D floats is
+// read by D/4 threads with 16-byte loads, and the 256/(D/4) thread groups
+// take every NG-th partition, four at a time, so the whole row set of a
+// (sequence, head) is in flight at once.  The groups' partial sums meet in
+// LDS.  With few partitions most groups would idle behind the barrier, so
+// the host picks this kernel only from kWideReduceParts partitions on.
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void reduce_wide_kernel(DecodeArgs a) {
+  using T = typename KV<DT>::T;
+  constexpr float kNegInf = -INFINITY;
+  constexpr int TPR = D / 4;               // threads per partition row
+  constexpr int NG = 256 / TPR;            // partition groups
+  constexpr int U = 4;                     // partitions per group in flight
+  __shared__ float4 gnum[NG][TPR];
+  __shared__ float gden[NG];
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int t = threadIdx.x;
+  const int grp = t / TPR;
+  const int c = t - grp * TPR;
+  const int ctx = clamp_ctx(a, s, BS);
+  const int nparts = part_range(a, s, 0, ctx, BS > 32 ? BS : 32).total;
+  if (nparts <= 1) return;
+  const size_t base = (static_cast<size_t>(s) * a.Hq + h) * a.pmax;
+  const float* mp = a.ws_m + base;
+  const float* lp = a.ws_l + base;
+  const float4* op = reinterpret_cast<const float4*>(a.ws_o + base * D) + c;
+  float M = kNegInf;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, mp[p]);
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  auto add = [&](const float4& v, float mk, float lk) {
+    const float sw = (mk == kNegInf) ? 0.f : fast_exp2(mk - M);
+    num.x = fmaf(v.x, sw, num.x);
+    num.y = fmaf(v.y, sw, num.y);
+    num.z = fmaf(v.z, sw, num.z);
+    num.w = fmaf(v.w, sw, num.w);
+    den = fmaf(lk, sw, den);
+  };
+  int p = grp;
+  for (; p + (U - 1) * NG < nparts; p += U * NG) {
+    float4 v[U];
+    float mk[U], lk[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      v[k] = op[static_cast<size_t>(p + k * NG) * TPR];
+      mk[k] = mp[p + k * NG];
+      lk[k] = lp[p + k * NG];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) add(v[k], mk[k], lk[k]);
+  }
+  for (; p < nparts; p += NG) add(op[static_cast<size_t>(p) * TPR], mp[p], lp[p]);
+  gnum[grp][c] = num;
+  if (c == 0) gden[grp] = den;
+  __syncthreads();
+  if (t < TPR) {
+    float4 nt = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dn = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      nt.x += gnum[k][t].x;
+      nt.y += gnum[k][t].y;
+      nt.z += gnum[k][t].z;
+      nt.w += gnum[k][t].w;
+      dn += gden[k];
+    }
+    const float inv = dn > 0.f ? 1.f / dn : 0.f;
+    T* o = static_cast<T*>(a.out) + (static_cast<size_t>(s) * a.Hq + h) * D + 4 * t;
+    o[0] = narrow<DT>(nt.x * inv);
+    o[1] = narrow<DT>(nt.y * inv);
+    o[2] = narrow<DT>(nt.z * inv);
+    o[3] = narrow<DT>(nt.w * inv);
+  }
+}
+
 template <int DT, int D, int BS, int G>
 int launch_decode(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_kernel<DT, D, BS, G>),
@@ -341,9 +419,11 @@ int launch_decode(const DecodeArgs& a, hipStream_t st) {
 
 template <int DT, int D, int BS>
 int launch_reduce(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((reduce_kernel<DT, D, BS>),
-                     dim3(static_cast<uint32_t>(a.Hq), static_cast<uint32_t>(a.S)), dim3(D), 0,
-                     st, a);
+  const dim3 grid(static_cast<uint32_t>(a.Hq), static_cast<uint32_t>(a.S));
+  if (a.pmax >= kWideReduceParts)
+    hipLaunchKernelGGL((reduce_wide_kernel<DT, D, BS>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<DT, D, BS>), grid, dim3(D), 0, st, a);
   return launch_status();
 }
 

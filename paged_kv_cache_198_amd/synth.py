@@ -37,8 +37,11 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 CONFIGS = {
     "tiny": dict(S=4, Hq=4, Hkv=4, D=64, dtype="f32", bs=16, NB=64,
                  lengths=("uniform", 1, 100), partition_tokens=0),
+    # Partitioning is a launch choice, not part of the workload's arithmetic:
+    # the 7B batch has 2048 (sequence, head) pairs with lognormal lengths, and
+    # splitting contexts into 512-token pieces evens out the workgroups.
     "llama7b": dict(S=64, Hq=32, Hkv=32, D=128, dtype="f16", bs=16, NB=16384,
-                    lengths=("lognormal", 500, 0.5, 16, 2048), partition_tokens=0),
+                    lengths=("lognormal", 500, 0.5, 16, 2048), partition_tokens=512),
     # NB is chosen per block size so that the pool holds 262144 tokens.
     "llama13b": dict(S=128, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16, NB=None,
                      pool_tokens=262144, lengths=("lognormal", 700, 0.5, 1, 2048),

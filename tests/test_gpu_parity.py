@@ -213,6 +213,22 @@ def test_dtype_head_dim_grid(dtype, D):
     check_decode(w, part=256)
 
 
+@pytest.mark.parametrize("name,over,part", [
+    # 16 or more partitions take the wide partition reduce; ragged counts
+    # (1, a few, many) in one batch, both head dims, every dtype, both kernels
+    ("long_gqa", dict(S=4, NB=2048, lengths=("fixed", [1, 33, 1100, 4000])), 64),
+    ("long_gqa", dict(S=3, NB=2048, bs=8, dtype="f16", lengths=("fixed", [4000, 17, 2049])), 32),
+    ("llama13b", dict(S=6, bs=16, pool_tokens=16384,
+                      lengths=("fixed", [1, 32, 33, 511, 512, 2048])), 32),
+    ("llama7b", dict(S=5, NB=512, Hq=4, Hkv=4, D=64, dtype="f32", lengths=("uniform", 1, 900)), 32),
+    ("llama7b", dict(S=5, NB=512, Hq=8, Hkv=2, dtype="f16", lengths=("uniform", 300, 1500)), 64),
+])
+def test_many_partitions(name, over, part):
+    w = synth.make_decode(name, device=DEV, **over)
+    assert -(-w.max_context_len // part) >= 16
+    check_decode(w, part=part)
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
