@@ -647,7 +647,7 @@ def run_beam(args, pa, synth, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "single-GPU benchmark: the decode path is not sharded over GPUs; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
