@@ -11,14 +11,16 @@
 namespace pa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
-// Tuning (measured on the 13B-shaped batch, see profiles/): 8 waves per
-// workgroup and 8 rows per lane per tile; non-temporal K/V loads raise the
-// achieved read bandwidth by about 12%.
+// Tuning (measured on the 13B- and 7B-shaped batches, see profiles/): 8
+// waves per workgroup and 4 rows per lane per tile (16 tokens per wave: 77
+// VGPRs, 6 waves per SIMD; 8 rows hold 113 VGPRs and allow 4, with more
+// bytes in flight per CU than the memory system serves best); non-temporal
+// K/V loads raise the achieved read bandwidth by about 12%.
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 8
 #endif
 #ifndef PA_DECODE_ROWS
-#define PA_DECODE_ROWS 8
+#define PA_DECODE_ROWS 4
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
