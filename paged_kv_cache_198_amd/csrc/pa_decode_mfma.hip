@@ -16,9 +16,12 @@
 //   * K and V rows are loaded coalesced (16 lanes x 16 B per 256-byte row)
 //     with raw buffer loads, one resource per block; rows past the context
 //     load zero without touching memory, so no load sits behind a branch.
-//     Two register stages keep the wavefront's next tile in flight while
-//     it uses the current one.  Small tiles keep the registers at about 150
-//     (three wavefronts per SIMD); workgroups of two wavefronts keep short
+//     A tile's K and V rows go to the wavefront's LDS rows as soon as they
+//     arrive.  In plain grouped-query decode the next tile's loads then go
+//     into the same registers, in flight while the tile is used (one
+//     register stage, about 125 VGPRs, four wavefronts per SIMD); work items,
+//     often only a few tiles long, keep two register stages (about 150,
+//     three wavefronts per SIMD).  Workgroups of two wavefronts keep short
 //     ranges from leaving wavefronts idle.
 //   * S^T = K . Q^T, one 16-token MFMA tile x 4 k-steps of 32 dims
 //     (v_mfma_f32_16x16x32): A = K through the wavefront's LDS tile (lane l:
@@ -31,9 +34,9 @@
 //     the accumulators are rarely rescaled.
 //   * O^T += V^T . P^T on v_mfma_f32_16x16x16 (K = the tile's 16 tokens):
 //     B = P^T is already where the scores left it (lane l: head l%16, tokens
-//     4(l/16) + i), A = V^T comes from the same LDS tile, now holding the V
-//     rows (rows padded to 272 bytes), through one transposing LDS read
-//     (ds_read_b64_tr_b16) per 16 dims.  The output rows of O^T are dims and
+//     4(l/16) + i), A = V^T comes from the tile's V rows in LDS (rows padded
+//     to 272 bytes) through one transposing LDS read (ds_read_b64_tr_b16)
+//     per 16 dims.  The output rows of O^T are dims and
 //     its columns heads, so lane l holds head l%16: the per-head rescale
 //     factor never leaves the lane.
 // Probabilities enter the second product rounded to the KV type; the running
@@ -77,7 +80,7 @@ struct TileRegs {
 // a suffix item has one member, the sequence itself.  Each column writes a
 // partial to its member's workspace slot, or, for slot -1, the final output.
 template <int DT, int BS, bool GROUP>
-__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(GROUP ? 3 : 4)))
 void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
@@ -95,7 +98,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
     float m[kMWaves][NC];
     float l[kMWaves][NC];
   };
-  constexpr int kTileBytes = kMWaves * kMTile * kVRow;
+  constexpr int kTileBytes = kMWaves * 2 * kMTile * kVRow;   // K and V rows per wavefront
   constexpr int kSmem = kTileBytes > static_cast<int>(sizeof(Merge)) ? kTileBytes : sizeof(Merge);
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   Merge& red = *reinterpret_cast<Merge*>(smem);
@@ -176,7 +179,8 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kMD * 2;
   const int last_lb = end > 0 ? (end - 1) / BS : 0;
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  char* vt = smem + w * (kMTile * kVRow);
+  char* kt = smem + w * (2 * kMTile * kVRow);   // the tile's K rows
+  char* vt = kt + kMTile * kVRow;               // and its V rows
 
   // Fused step: the last partition owns position ctx-1.  Its new K/V rows of
   // head g come from the inputs (loaded here with the query; lane (n, q)
@@ -234,17 +238,27 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // Scores, online softmax and the V product for the tile at t0 (< end).
-  constexpr int NU = kMTile / 16;          // 16-token score sub-tiles
-  auto consume = [&](int t0, const Tile& tl) {
-    // K rows through LDS into the A-operand layout: lane (n, q) of sub-tile
-    // u takes 16 bytes of token 16u + n at dims 32kk + 8q.
+  // The tile's K and V rows go to the wavefront's LDS rows as soon as they
+  // arrive (the new token's row, if the tile holds it, over its row), which
+  // frees the load registers for the next tile's loads.
+  auto stage = [&](int t0, const Tile& tl) {
 #pragma unroll
-    for (int j = 0; j < kMRowGroups; ++j)
-      *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.kr[j];
-    const bool has_new = append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile;
-    if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nk;
-    lds_order();
+    for (int j = 0; j < kMRowGroups; ++j) {
+      *reinterpret_cast<uint4*>(kt + (4 * j + q) * kVRow + 16 * n) = tl.kr[j];
+      *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
+    }
+    if (append && t0 <= ctx - 1 && ctx - 1 < t0 + kMTile && q == 0) {
+      *reinterpret_cast<uint4*>(kt + (ctx - 1 - t0) * kVRow + 16 * n) = nk;
+      *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nv;
+    }
+  };
+
+  // Scores, online softmax and the V product for the staged tile at t0
+  // (< end); bok are its blocks' pool flags.
+  constexpr int NU = kMTile / 16;          // 16-token score sub-tiles
+  auto consume = [&](int t0, const bool (&bok)[NBK]) {
+    // A operand: lane (n, q) of sub-tile u takes 16 bytes of token 16u + n
+    // at dims 32kk + 8q.
     f32x4_t sc[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -252,11 +266,10 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint4 ka =
-            *reinterpret_cast<const uint4*>(vt + (16 * u + n) * kVRow + 64 * kk + 16 * q);
+            *reinterpret_cast<const uint4*>(kt + (16 * u + n) * kVRow + 64 * kk + 16 * q);
         sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
       }
     }
-    lds_order();
     float sv[4 * NU];
     float mt = kNegInf;
 #pragma unroll
@@ -265,7 +278,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int rel = 16 * u + 4 * q + i;
         const bool ok = t0 + rel < end &&
-                        pick_ok(tl.bok, (BS > kMTile ? t0 % BS + rel : rel) / BS);
+                        pick_ok(bok, (BS > kMTile ? t0 % BS + rel : rel) / BS);
         const float x = ok ? sc[u][i] * a.qscale : kNegInf;
         sv[4 * u + i] = x;
         mt = fmaxf(mt, x);
@@ -295,13 +308,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
     }
     l_run += psum;
 
-    // V rows to LDS (over the K rows, whose reads are done), then read back
-    // transposed.
-#pragma unroll
-    for (int j = 0; j < kMRowGroups; ++j)
-      *reinterpret_cast<uint4*>(vt + (4 * j + q) * kVRow + 16 * n) = tl.vr[j];
-    if (has_new && q == 0) *reinterpret_cast<uint4*>(vt + (ctx - 1 - t0) * kVRow + 16 * n) = nv;
-    lds_order();
+    // V^T read back transposed from the V rows
     if constexpr (NU == 2) {
       u16x8_t pb;
 #pragma unroll
@@ -317,30 +324,56 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       for (int dt = 0; dt < 8; ++dt)
         o[dt] = mma16<DT>(vt_operand16(vt, kVRow, dt, n, q), pb, o[dt]);
     }
-    lds_order();                           // the next tile rewrites these rows
   };
 
   constexpr int kStride = kMWaves * kMTile;
-  {
-    // Two register stages: the loads of the wavefront's next tile are in
-    // flight while it waits for, and then uses, the current one.
-    // The loads are issued without conditions (a tile past the end loads
-    // zeros without touching memory), so the compiler can count the loads
-    // in flight on every path and wait only for the ones each use needs.
-    Tile ta, tb;
-    const int first = start + wv * kMTile;
-    issue(first, ta);
-    issue(first + kStride, tb);
-    // The query and new-row loads, issued before the tiles', are waited for
-    // here, where the tile loads stay in flight.
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int first = start + wv * kMTile;
+  // The query and new-row loads, issued before the tiles', are waited for
+  // after the first tile loads are issued, so those stay in flight.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  auto wait_query = [&]() {
     asm volatile("" ::"v"(qt[0]), "v"(qt[1]), "v"(qt[2]), "v"(qt[3]),
                  "v"(__builtin_bit_cast(u32x4_t, nk)), "v"(__builtin_bit_cast(u32x4_t, nv)));
+  };
+  // The loads are issued without conditions (a tile past the end loads zeros
+  // without touching memory), so the compiler can count the loads in flight
+  // on every path and wait only for the ones each use needs.
+  if constexpr (!GROUP) {
+    // One register stage: the next tile's loads go into the registers the
+    // current tile has just left for LDS, and are in flight while it is
+    // used.  About 125 VGPRs: 4 wavefronts per SIMD.
+    Tile ta;
+    issue(first, ta);
+    wait_query();
+    for (int t0 = first; t0 < end; t0 += kStride) {
+      stage(t0, ta);
+      bool bok[NBK];
+#pragma unroll
+      for (int b = 0; b < NBK; ++b) bok[b] = ta.bok[b];
+      issue(t0 + kStride, ta);
+      lds_order();
+      consume(t0, bok);
+      lds_order();                         // the next tile rewrites these rows
+    }
+  } else {
+    // Two register stages: work items are often a few tiles long, and the
+    // tile after next is already in flight when a wavefront starts a tile.
+    // About 150 VGPRs: 3 wavefronts per SIMD.
+    Tile ta, tb;
+    issue(first, ta);
+    issue(first + kStride, tb);
+    wait_query();
     for (int t0 = first; t0 < end; t0 += 2 * kStride) {
-      consume(t0, ta);
+      stage(t0, ta);
+      lds_order();
+      consume(t0, ta.bok);
+      lds_order();
       issue(t0 + 2 * kStride, ta);
       if (t0 + kStride >= end) break;
-      consume(t0 + kStride, tb);
+      stage(t0 + kStride, tb);
+      lds_order();
+      consume(t0 + kStride, tb.bok);
+      lds_order();
       issue(t0 + 3 * kStride, tb);
     }
   }
