@@ -1151,16 +1151,17 @@ def test_engine_chunked_prefill_with_registry():
     assert kv.alloc.export() == (list(oa_.ref), oa_.free_stack())
 
 
-@pytest.mark.parametrize("extra", [0, 3])
-def test_read_probe_reads_every_chunk(extra):
-    # 1 MiB (+ extra 16-byte chunks, a slice cut short): workgroup b reads the
-    # 32 KB slices b, b + 4096, ...; thread t of it reads chunks
-    # slice + 256 u + t (u = 0..7) and stores the XOR of all their words
+@pytest.mark.parametrize("extra,grid", [(0, 4096), (3, 4096), (3, 256), (3, 16)])
+def test_read_probe_reads_every_chunk(extra, grid):
+    # 1 MiB (+ extra 16-byte chunks, a slice cut short) with `grid`
+    # workgroups: workgroup b reads the 32 KB slices b, b + grid, ...; thread
+    # t of it reads chunks slice + 256 u + t (u = 0..7) of each and stores the
+    # XOR of all their words (grid 16: several slices per workgroup)
     n16 = (1 << 16) + extra
     g = torch.Generator(device=DEV)
     g.manual_seed(5)
     src = torch.randint(-2**31, 2**31 - 1, (4 * n16,), generator=g, device=DEV, dtype=torch.int32)
-    out = torch.full((4096 * 256,), -1, dtype=torch.int32, device=DEV)
+    out = torch.full((grid * 256,), -1, dtype=torch.int32, device=DEV)
     pa.pa_probe_read_bandwidth(src, out)
     torch.cuda.synchronize()
     w = src.cpu().numpy().view(np.uint32).reshape(-1, 4)
@@ -1168,6 +1169,8 @@ def test_read_probe_reads_every_chunk(extra):
     slices = -(-n16 // 2048)
     padded = np.zeros(slices * 2048, dtype=np.uint32)
     padded[:n16] = fold
-    expect = np.zeros(4096 * 256, dtype=np.uint32)
-    expect[:slices * 256] = np.bitwise_xor.reduce(padded.reshape(slices, 8, 256), axis=1).reshape(-1)
-    assert np.array_equal(out.cpu().numpy().view(np.uint32), expect)
+    per_slice = np.bitwise_xor.reduce(padded.reshape(slices, 8, 256), axis=1)
+    expect = np.zeros((grid, 256), dtype=np.uint32)
+    for k in range(slices):
+        expect[k % grid] ^= per_slice[k]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), expect.reshape(-1))
