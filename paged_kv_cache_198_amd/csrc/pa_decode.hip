@@ -334,9 +334,9 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
 // The same combination for many partitions (long contexts).  One workgroup
 // of 256 threads per (query head, sequence): a partition's row of D floats is
 // read by D/4 threads with 16-byte loads, and the 256/(D/4) thread groups
-// take every NG-th partition, four at a time, so the whole row set of a
-// (sequence, head) is in flight at once.  The groups' partial sums meet in
-// LDS.  With few partitions most groups would idle behind the barrier, so
+// take every NG-th partition, four at a time, so 4 NG partition rows of a
+// (sequence, head) are in flight at once (32 at D = 128, 64 at D = 64).  The
+// groups' partial sums meet in LDS.  With few partitions most groups would idle behind the barrier, so
 // the host picks this kernel only from kWideReduceParts partitions on.
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(256) void reduce_wide_kernel(DecodeArgs a) {
