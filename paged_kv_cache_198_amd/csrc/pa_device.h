@@ -12,15 +12,16 @@ namespace pa {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 // Tuning (measured on the 13B- and 7B-shaped batches, see profiles/): 8
-// waves per workgroup and 4 rows per lane per tile (16 tokens per wave: 77
-// VGPRs, 6 waves per SIMD; 8 rows hold 113 VGPRs and allow 4, with more
-// bytes in flight per CU than the memory system serves best); non-temporal
-// K/V loads raise the achieved read bandwidth by about 12%.
+// waves per workgroup and 3 rows per lane per tile (12 tokens per wave at
+// D = 128, 2 bytes: 68 VGPRs, 3 workgroups per CU; 8 rows hold 113 VGPRs and
+// allow 2, with more bytes in flight per CU than the memory system serves
+// best); non-temporal K/V loads raise the achieved read bandwidth by about
+// 12%.
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 8
 #endif
 #ifndef PA_DECODE_ROWS
-#define PA_DECODE_ROWS 4
+#define PA_DECODE_ROWS 3
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
