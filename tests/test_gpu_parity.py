@@ -1174,3 +1174,39 @@ def test_read_probe_reads_every_chunk(extra, grid):
     for k in range(slices):
         expect[k % grid] ^= per_slice[k]
     assert np.array_equal(out.cpu().numpy().view(np.uint32), expect.reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# seeded random configurations: dtype, head dim, group size, KV heads, block
+# size, ragged lengths and partition size drawn together, through both the
+# fused step and the two-call path
+# ---------------------------------------------------------------------------
+def _random_config(i):
+    import random
+    r = random.Random(7000 + i)
+    dtype = r.choice(["f32", "f16", "bf16"])
+    D = r.choice([64, 128])
+    G = r.choice([1, 2, 4, 8])
+    Hkv = r.choice([1, 2, 3, 4])
+    bs = r.choice([8, 16, 32, 64, 128])
+    S = r.randint(1, 6)
+    hi = r.choice([40, 300, 1500, 4000])
+    lens = [r.randint(1, hi) for _ in range(S)]
+    NB = max(64, sum(-(-n // bs) for n in lens) + r.randint(0, 64))
+    part = r.choice([0, bs * r.randint(1, 8), (32 if bs <= 32 else bs) * r.randint(1, 16)])
+    return dtype, D, G, Hkv, bs, lens, NB, part
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configurations(i):
+    dtype, D, G, Hkv, bs, lens, NB, part = _random_config(i)
+    note(f"case random {i}: {dtype} D={D} G={G} Hkv={Hkv} bs={bs} lens={lens} NB={NB} part={part}")
+    w = synth.make_decode("llama7b", device=DEV, S=len(lens), Hq=Hkv * G, Hkv=Hkv, D=D,
+                          dtype=dtype, bs=bs, NB=NB, lengths=("fixed", lens), seed=8000 + i)
+    ref, _ = oracle_step(w)
+    out1, _, _, _ = run_step(w, part)
+    out2, _, _ = run_fused(w, part)
+    assert torch.equal(bits(out1), bits(out2))
+    err = float(np.max(np.abs(widened(out1, dtype) - ref)))
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
