@@ -423,8 +423,17 @@ def run_prefill(args, pa, synth, torch):
     flops per step = sum over prompt rows and query heads of 4 D (p + 1)
     (two products over the p + 1 attended keys)."""
     w = synth.make_prefill(seed=args.seed, device="cuda", bs=args.bs)
-    slots = torch.from_numpy(w.slots()).to("cuda")
-    tables = torch.from_numpy(w.block_tables).to("cuda")
+    # slots and tables from the library's allocator: each prompt grows to its
+    # length in a pool handing out blocks in the workload's order
+    alloc = pa.Allocator(w.NB, w.bs, init_order=w.block_order)
+    rows = []
+    for s in range(w.S):
+        alloc.create(s)
+        sl, _, _ = alloc.append_n(s, int(w.context_lens[s]))
+        rows.append(sl[len(sl) - int(w.chunk_lens[s]):])
+    tables_h, _ = alloc.build_batch(list(range(w.S)), w.MB)
+    slots = torch.from_numpy(np.concatenate(rows)).to("cuda")
+    tables = torch.from_numpy(tables_h).to("cuda")
     lens = torch.from_numpy(w.context_lens).to("cuda")
     qs = torch.from_numpy(w.query_start).to("cuda")
     kc, vc = w.key_cache, w.value_cache

@@ -471,6 +471,7 @@ class PrefillWorkload:
     context_lens: np.ndarray     # int32 [S] prefix + chunk
     query_start: np.ndarray      # int32 [S+1] packed row offsets of the chunks
     block_tables: np.ndarray     # int32 [S, MB]
+    block_order: np.ndarray      # int32 [NB] the permutation the tables were cut from
     q: torch.Tensor              # [T, Hq, D]
     key_cache: torch.Tensor      # [NB, Hkv, bs, D]: prefixes stored, the rest NaN
     value_cache: torch.Tensor
@@ -485,16 +486,6 @@ class PrefillWorkload:
     def MB(self) -> int:
         return int(self.block_tables.shape[1])
 
-    def slots(self) -> np.ndarray:
-        """Slot of every chunk row (int64 [T]), from the block tables."""
-        out = []
-        for s in range(self.S):
-            pre = int(self.context_lens[s]) - int(self.chunk_lens[s])
-            for i in range(int(self.chunk_lens[s])):
-                p = pre + i
-                out.append(int(self.block_tables[s, p // self.bs]) * self.bs + p % self.bs)
-        return np.asarray(out, dtype=np.int64)
-
 
 def make_prefill(seed: int = 0, device="cpu", **over) -> PrefillWorkload:
     cfg = dict(PREFILL)
@@ -505,7 +496,7 @@ def make_prefill(seed: int = 0, device="cpu", **over) -> PrefillWorkload:
     prefix = draw_lengths(rng, cfg["prefix"], S)
     chunk = draw_lengths(rng, cfg["chunk"], S)
     ctx = (prefix + chunk).astype(np.int32)
-    tables, _ = paged_tables(rng, ctx, bs, NB, cfg.get("MB"))
+    tables, perm = paged_tables(rng, ctx, bs, NB, cfg.get("MB"))
     mask = filled_mask(tables, prefix.astype(np.int64), bs, NB)
     gen = _generator(seed, device)
     dt = cfg["dtype"]
@@ -523,8 +514,9 @@ def make_prefill(seed: int = 0, device="cpu", **over) -> PrefillWorkload:
     qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
     return PrefillWorkload(seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, dtype=dt,
                            scale=float(np.float32(1.0 / np.sqrt(D))), chunk_lens=chunk,
-                           context_lens=ctx, query_start=qs, block_tables=tables, q=q,
-                           key_cache=pools[0], value_cache=pools[1], new_key=nk, new_value=nv)
+                           context_lens=ctx, query_start=qs, block_tables=tables,
+                           block_order=perm, q=q, key_cache=pools[0], value_cache=pools[1],
+                           new_key=nk, new_value=nv)
 
 
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
