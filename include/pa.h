@@ -141,11 +141,12 @@ int pa_decode_attention(void* out, const void* query,
  * keys and values are gathered from the blocks).  For every sequence s with
  * c = context_lens[s] >= 1, key[s] / value[s] ([Hkv][D]) are stored at
  * logical position c-1, i.e. block block_tables[s][(c-1)/bs], offset
- * (c-1)%bs (skipped if that entry is outside [0, NB)), and out[s] is the
- * attention over c tokens including the new one.  The result, pools
- * included, is bit-identical to pa_reshape_and_cache with those slots
- * followed by pa_decode_attention; one launch is saved and the new rows are
- * used from registers rather than read back.
+ * (c-1)%bs (skipped if (c-1)/bs >= MB or that entry is outside [0, NB)),
+ * and out[s] is the attention over the first min(c, max_context_len, MB*bs)
+ * tokens, which includes the new one unless c was clamped.  The result,
+ * pools included, is bit-identical to pa_reshape_and_cache with those slots
+ * (-1 where skipped) followed by pa_decode_attention; one launch is saved
+ * and the new rows are used from registers rather than read back.
  *   key, value       device, [S][Hkv][D] of `dtype`.
  *   key_cache,
  *   value_cache      device, written at the S new slots only.
@@ -262,7 +263,9 @@ size_t pa_cascade_workspace_bytes(int32_t S, int32_t Hq, int32_t D, int32_t slot
  *   slots_max        info[0..1] of the plan.
  *   key, value       device [S][Hkv][D] new rows, or both NULL for
  *                    attention only; the row is stored by the item that
- *                    ends at the sequence's last position.
+ *                    ends at the sequence's last position.  A sequence whose
+ *                    length is clamped (context_lens[s] above
+ *                    max_context_len or MB*bs) gets no store.
  *   partition_tokens as given to pa_cascade_plan.
  *   workspace        device, pa_cascade_workspace_bytes(...) bytes,
  *                    256-byte aligned; may be NULL when that size is 0.

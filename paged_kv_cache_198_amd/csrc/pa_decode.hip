@@ -113,11 +113,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int last_lb = end > 0 ? (end - 1) / BS : 0;
   const int wv = __builtin_amdgcn_readfirstlane(w);
 
-  // Fused step: this workgroup owns position ctx-1 (the last partition).
-  // In the tile that holds the position, the lanes of its row take the new
-  // K/V rows of head g from the inputs instead of the pool and store them
-  // into the slot.
-  const bool append = a.new_key != nullptr && ctx > 0 && p == nparts - 1;
+  // Fused step: the last partition owns the new token at position c-1,
+  // c = context_lens[s].  When c is the attended length (not clamped), the
+  // lanes of that row, in the tile that holds it, take the new K/V rows of
+  // head g from the inputs instead of the pool and store them into the slot.
+  // A clamped length attends fewer tokens; the row is then only stored, after
+  // the loop, as a separate cache write would store it.
+  const int raw_ctx = a.context_lens[s];
+  const bool owns_new = a.new_key != nullptr && raw_ctx > 0 && p == nparts - 1;
+  const bool append = owns_new && raw_ctx == ctx;
 
   for (int t0 = start + wv * TILE; t0 < end; t0 += kWaves * TILE) {
     size_t off[NL];
@@ -215,6 +219,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       for (int gi = 0; gi < G; ++gi)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[gi][e] = fmaf(pw[j][gi], vf[e], acc[gi][e]);
+    }
+  }
+
+  if (owns_new && raw_ctx > ctx && w == 0 && r == 0) {
+    // the new token lies past the attended range: store only
+    const int pos = raw_ctx - 1;
+    if (pos / BS < a.MB) {
+      const int blk = trow[pos / BS];
+      if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB)) {
+        const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * D * EB + c * 16;
+        const size_t dst = static_cast<size_t>(blk) * bstride +
+                           static_cast<size_t>(pos % BS) * (D * EB) + c * 16;
+        *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_key) + src);
+        *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) =
+            *reinterpret_cast<const uint4*>(static_cast<const char*>(a.new_value) + src);
+      }
     }
   }
 

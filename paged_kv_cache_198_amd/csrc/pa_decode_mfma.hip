@@ -182,19 +182,26 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   char* kt = smem + w * (2 * kMTile * kVRow);   // the tile's K rows
   char* vt = kt + kMTile * kVRow;               // and its V rows
 
-  // Fused step: the last partition owns position ctx-1.  Its new K/V rows of
-  // head g come from the inputs (loaded here with the query; lane (n, q)
-  // holds bytes 16n .. 16n+15), replace that row of the tile in LDS, and are
-  // stored into the slot after the loop.  Without a new token the loads go
-  // through an empty resource and return zeros.
-  const bool append = a.new_key != nullptr && ctx > 0 && (GROUP ? owns_last : p == nparts - 1);
+  // Fused step: the last partition owns the new token at position c-1,
+  // c = context_lens[s].  Its K/V rows of head g come from the inputs
+  // (loaded here with the query; lane (n, q) holds bytes 16n .. 16n+15) and
+  // are stored into the slot after the loop; when c is the attended length
+  // (not clamped) they also replace that row of the tile in LDS.  A plain
+  // decode with a clamped length stores the row without attending it, as a
+  // separate cache write would; a work item stores it only when c is not
+  // clamped.  Without a new token the loads go through an empty resource and
+  // return zeros.
+  const int raw_ctx = a.context_lens[s];
+  const bool owns_new = a.new_key != nullptr && raw_ctx > 0 &&
+                        (GROUP ? owns_last && raw_ctx == ctx : p == nparts - 1);
+  const bool append = owns_new && raw_ctx == ctx;
   uint4 nk, nv;
   {
     const size_t src = (static_cast<size_t>(s) * a.Hkv + g) * kMD * 2;
-    const uint32_t nbytes = append ? static_cast<uint32_t>(kMD * 2) : 0u;
-    nk = buffer_load16(make_rsrc(append ? static_cast<const char*>(a.new_key) + src : kb, nbytes),
+    const uint32_t nbytes = owns_new ? static_cast<uint32_t>(kMD * 2) : 0u;
+    nk = buffer_load16(make_rsrc(owns_new ? static_cast<const char*>(a.new_key) + src : kb, nbytes),
                        16u * n);
-    nv = buffer_load16(make_rsrc(append ? static_cast<const char*>(a.new_value) + src : vb, nbytes),
+    nv = buffer_load16(make_rsrc(owns_new ? static_cast<const char*>(a.new_value) + src : vb, nbytes),
                        16u * n);
   }
 
@@ -382,11 +389,13 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   // through the pool pointers could alias the table as far as the compiler
   // knows, and a vector load of a table entry would have to wait for every
   // tile load issued before it).  Only this workgroup reads that slot.
-  if (append && ctx - 1 >= start && ctx - 1 < end && wv == 0 && q == 0) {
-    const int blk = table_entry(trow, (ctx - 1) / BS);
+  if (owns_new && (!append || (ctx - 1 >= start && ctx - 1 < end)) && wv == 0 && q == 0 &&
+      (raw_ctx - 1) / BS < a.MB) {
+    const int pos = raw_ctx - 1;
+    const int blk = table_entry(trow, pos / BS);
     if (static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB)) {
       const size_t dst = static_cast<size_t>(blk) * bstride +
-                         static_cast<size_t>((ctx - 1) % BS) * (kMD * 2) + 16 * n;
+                         static_cast<size_t>(pos % BS) * (kMD * 2) + 16 * n;
       *reinterpret_cast<uint4*>(const_cast<char*>(kb) + dst) = nk;
       *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
     }

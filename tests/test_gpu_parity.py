@@ -19,6 +19,7 @@ import oracle.alloc as oa
 import oracle.decode as od
 import paged_kv_cache_198_amd as pa
 from paged_kv_cache_198_amd import synth
+from prefill_slots import lib_prefill_slots, oracle_prefill_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -571,6 +572,68 @@ def test_fused_step_against_oracle():
     assert err <= TOL[w.dtype]
 
 
+CLAMP_CASES = [  # vector-ALU and matrix-core kernels, single pass and partitioned
+    ("llama13b", dict(bs=16, S=6, pool_tokens=16384), 0),
+    ("llama13b", dict(bs=8, S=6, pool_tokens=16384), 256),
+    ("llama7b", dict(S=5, NB=512, Hq=8, Hkv=2, D=64, dtype="f16", lengths=("uniform", 40, 900)), 0),
+    ("long_gqa", dict(S=4, NB=1024, lengths=("uniform", 700, 4000)), 512),
+    ("long_gqa", dict(S=4, NB=1024, bs=32, dtype="f16", lengths=("uniform", 100, 3000)), 0),
+]
+
+
+@pytest.mark.parametrize("name,over,part", CLAMP_CASES)
+def test_fused_step_clamped_lengths(name, over, part):
+    """Lengths above max_context_len, and one past the table's reach: the
+    fused step stores each new row where a separate cache write would (none
+    for the one past the table) and attends the clamped range; outputs and
+    whole pools equal the two-call path bit for bit, and the oracle's own
+    cache write and decode over the clamped lengths."""
+    w = synth.make_decode(name, device=DEV, **over)
+    step, tables, lens = lib_slots(w)
+    order = np.argsort(w.context_lens)
+    big = int(order[-1])                          # its length goes past the table
+    # clamps the longer half; the long one's clamped range holds filled rows
+    cap = min(int(w.context_lens[order[len(order) // 2]]), int(w.context_lens[big]) - 1)
+    lens2 = lens.copy()
+    lens2[big] = w.MB * w.bs + 3
+    slots = step.copy()
+    slots[big] = -1                               # no slot exists past the table
+    note(f"case clamp {name} {over} part={part} cap={cap} lens={lens2.tolist()}")
+    t_d, l_d = torch.from_numpy(tables).to(DEV), torch.from_numpy(lens2).to(DEV)
+    ws = pa.make_workspace(w.S, w.Hq, w.D, cap, part)
+    kc1, vc1 = w.key_cache.clone(), w.value_cache.clone()
+    out1 = torch.full((w.S, w.Hq, w.D), float("nan"), dtype=w.q.dtype, device=DEV)
+    pa.pa_reshape_and_cache(w.new_key, w.new_value, kc1, vc1, torch.from_numpy(slots).to(DEV))
+    pa.pa_decode_attention(out1, w.q, kc1, vc1, t_d, l_d, cap, w.scale, part, ws)
+    kc2, vc2 = w.key_cache.clone(), w.value_cache.clone()
+    out2 = torch.full_like(out1, float("nan"))
+    pa.pa_decode_step(out2, w.q, w.new_key, w.new_value, kc2, vc2, t_d, l_d, cap, w.scale,
+                      part, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out1), bits(out2))
+    assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+    # the oracle: slot of position c-1 through the table where it exists,
+    # then attention over min(c, cap, MB*bs) tokens
+    oslots = [od.slot_of(w.block_tables[s], int(lens2[s]) - 1, w.bs)
+              if (int(lens2[s]) - 1) // w.bs < w.MB else -1 for s in range(w.S)]
+    assert np.array_equal(np.asarray(oslots, dtype=np.int64), slots)
+    okc, ovc = od.reshape_and_cache(synth.to_numpy_storage(w.new_key),
+                                    synth.to_numpy_storage(w.new_value),
+                                    synth.to_numpy_storage(w.key_cache),
+                                    synth.to_numpy_storage(w.value_cache), oslots)
+    u8 = lambda a: np.ascontiguousarray(a).view(np.uint8)    # NaN poison compares too
+    assert np.array_equal(u8(synth.to_numpy_storage(kc2)), u8(okc))
+    assert np.array_equal(u8(synth.to_numpy_storage(vc2)), u8(ovc))
+    att = np.minimum(lens2, min(cap, w.MB * w.bs))
+    ref = od.paged_decode(synth.to_numpy_storage(w.q), okc, ovc, w.block_tables, att, w.scale,
+                          w.dtype)
+    got = widened(out2, w.dtype)
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    note(f"  max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
 # ---------------------------------------------------------------------------
 # the engine (allocator + kernels sequenced in Python) against the oracle's own
 # drive of the same shared-prefix script
@@ -951,7 +1014,7 @@ def run_prefill_lib(w, context_lens=None, max_query_len=None):
     kc, vc = w.key_cache.clone(), w.value_cache.clone()
     if w.T:
         pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc,
-                                torch.from_numpy(w.slots()).to(DEV))
+                                torch.from_numpy(lib_prefill_slots(w)).to(DEV))
     out = torch.full((max(w.T, 1), w.Hq, w.D), float("nan"), dtype=w.q.dtype, device=DEV)[:w.T]
     mq = int(w.chunk_lens.max()) if max_query_len is None else max_query_len
     pa.pa_prefill_attention(out, w.q, kc, vc, torch.from_numpy(w.block_tables).to(DEV),
@@ -966,7 +1029,8 @@ def prefill_oracle(w, context_lens=None, seqs=None):
     kc, vc = od.reshape_and_cache(synth.to_numpy_storage(w.new_key),
                                   synth.to_numpy_storage(w.new_value),
                                   synth.to_numpy_storage(w.key_cache),
-                                  synth.to_numpy_storage(w.value_cache), w.slots())
+                                  synth.to_numpy_storage(w.value_cache),
+                                  oracle_prefill_slots(w))
     out = od.paged_prefill(synth.to_numpy_storage(w.q), kc, vc, w.block_tables, lens,
                            w.query_start, w.scale, w.dtype, seqs=seqs)
     return out, kc, vc
@@ -995,6 +1059,7 @@ def test_prefill_against_oracle(G, Hkv, bs, dtype, prefix, chunk):
                            pool_tokens=32768, prefix=prefix, chunk=chunk)
     note(f"case prefill G={G} Hkv={Hkv} bs={bs} {dtype} chunks={w.chunk_lens.tolist()} "
          f"ctx={w.context_lens.tolist()}")
+    assert np.array_equal(lib_prefill_slots(w), oracle_prefill_slots(w))   # slots bit-exact
     out, kc, vc = run_prefill_lib(w)
     ref, rkc, rvc = prefill_oracle(w)
     assert np.array_equal(synth.to_numpy_storage(kc).view(np.uint16), rkc.view(np.uint16))
@@ -1041,7 +1106,8 @@ def test_prefill_table_entry_outside_pool():
     bad[0, 1] = w.NB + 3
     bad[2, 0] = -7
     kc, vc = w.key_cache.clone(), w.value_cache.clone()
-    pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc, torch.from_numpy(w.slots()).to(DEV))
+    pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc,
+                            torch.from_numpy(lib_prefill_slots(w)).to(DEV))
     out = torch.empty_like(w.q)
     pa.pa_prefill_attention(out, w.q, kc, vc, torch.from_numpy(bad).to(DEV),
                             torch.from_numpy(w.context_lens).to(DEV),
