@@ -60,7 +60,8 @@ enum {
   PA_ERR_OOM = -2,         /* allocator has no free block; state unchanged  */
   PA_ERR_HIP = -3,         /* HIP reported an error for a launch            */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required    */
-  PA_ERR_UNSUPPORTED = -5  /* valid shape outside the compiled set          */
+  PA_ERR_UNSUPPORTED = -5, /* valid shape outside the compiled set          */
+  PA_ERR_TOO_LARGE = -6    /* needs more than the static scratch holds      */
 };
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -160,6 +161,29 @@ int pa_decode_step(void* out, const void* query, const void* key, const void* va
                    int32_t partition_tokens,
                    void* workspace, size_t workspace_bytes,
                    int32_t dtype, void* stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pa_decode_step with the
+ * split-context workspace taken from a static device array of
+ * PA_STATIC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends; the call allocates nothing and takes no
+ * workspace argument.  Returns PA_ERR_TOO_LARGE, having enqueued nothing,
+ * when pa_decode_workspace_bytes(S, Hq, D, min(max_context_len, MB*bs),
+ * partition_tokens) exceeds that size (e.g. 8 sequences x 64 query heads x
+ * 32768 tokens in 512-token partitions need 17 MB).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and give unspecified results; calls on one
+ * stream are ordered.  The array needs no clearing: each launch writes every
+ * partial it reads.  The stream must belong to the current device.  Every
+ * other argument, the result and the supported set as for pa_decode_step. */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_step_noalloc(void* out, const void* query, const void* key, const void* value,
+                           void* key_cache, void* value_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t bs, int32_t NB, int32_t MB,
+                           int32_t max_context_len, float scale,
+                           int32_t partition_tokens, int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Paged prefill attention: causal attention for a chunk of new tokens per

@@ -31,6 +31,8 @@ _ELEM = {PA_F32: 4, PA_F16: 2, PA_BF16: 2}
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNSUPPORTED = (
     0, -1, -2, -3, -4, -5)
+PA_ERR_TOO_LARGE = -6
+PA_STATIC_SCRATCH_BYTES = 32 << 20   # the no-alloc step's static workspace per GPU
 
 _lib = None
 
@@ -51,6 +53,9 @@ _SIGNATURES = {
     "pa_decode_step": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
                                 _c_i32, _c_p, ctypes.c_size_t, _c_i32, _c_p]),
+    "pa_decode_step_noalloc": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        ctypes.c_float, _c_i32, _c_i32, _c_p]),
     "pa_cascade_plan": (_c_int, [_p_i32, _p_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _p_i32, ctypes.c_size_t, _p_i32]),
     "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_c_i32, _c_i32, _c_i32, _c_i32]),
@@ -213,13 +218,8 @@ def pa_decode_attention(out: torch.Tensor, query: torch.Tensor, key_cache: torch
     _check(rc, "pa_decode_attention")
 
 
-def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
-                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
-                   context_lens: torch.Tensor, max_context_len: int, scale: float,
-                   partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> None:
-    """Fused step: store key[s]/value[s] ([S, Hkv, D]) at position
-    context_lens[s]-1 of each sequence and attend over its whole context."""
+def _step_shapes(out, query, key, value, key_cache, value_cache, block_tables, context_lens):
+    """Checks the fused step's tensors; (dtype code, S, Hq, Hkv, D, bs, NB, MB)."""
     dt = _kv_dtype(key_cache)
     NB, Hkv, bs, D = key_cache.shape
     S, Hq, Dq = query.shape
@@ -236,7 +236,18 @@ def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, va
         raise ValueError("block_tables must be [S, MB]")
     if tuple(context_lens.shape) != (S,):
         raise ValueError("context_lens must be [S]")
-    MB = block_tables.shape[1]
+    return dt, S, Hq, Hkv, D, bs, NB, block_tables.shape[1]
+
+
+def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, max_context_len: int, scale: float,
+                   partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Fused step: store key[s]/value[s] ([S, Hkv, D]) at position
+    context_lens[s]-1 of each sequence and attend over its whole context."""
+    dt, S, Hq, Hkv, D, bs, NB, MB = _step_shapes(out, query, key, value, key_cache, value_cache,
+                                                 block_tables, context_lens)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")
@@ -249,6 +260,25 @@ def pa_decode_step(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, va
         int(max_context_len), float(scale), int(partition_tokens), ws_ptr, ws_bytes, dt,
         _stream(stream))
     _check(rc, "pa_decode_step")
+
+
+def pa_decode_step_noalloc(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                           value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float, partition_tokens: int = 0,
+                           stream=None) -> None:
+    """The fused step with no workspace argument: partials go to the
+    library's static per-GPU scratch (PA_STATIC_SCRATCH_BYTES); raises
+    PaError(PA_ERR_TOO_LARGE) when the launch would need more."""
+    dt, S, Hq, Hkv, D, bs, NB, MB = _step_shapes(out, query, key, value, key_cache, value_cache,
+                                                 block_tables, context_lens)
+    rc = lib().pa_decode_step_noalloc(
+        _dev(out, "out"), _dev(query, "query"), _dev(key, "key"), _dev(value, "value"),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32),
+        _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, bs, NB, MB,
+        int(max_context_len), float(scale), int(partition_tokens), dt, _stream(stream))
+    _check(rc, "pa_decode_step_noalloc")
 
 
 def make_workspace(S: int, Hq: int, D: int, max_context_len: int, partition_tokens: int,

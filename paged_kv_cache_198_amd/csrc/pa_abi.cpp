@@ -11,6 +11,7 @@ extern "C" const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "HIP launch error";
     case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case PA_ERR_UNSUPPORTED: return "shape or type outside the compiled set";
+    case PA_ERR_TOO_LARGE: return "workspace needed exceeds the static scratch";
     default: return "unknown status";
   }
 }

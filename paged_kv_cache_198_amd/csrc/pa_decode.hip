@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_device.h"
@@ -676,4 +677,65 @@ extern "C" int pa_decode_cascade(void* out, const void* query, const void* key,
   return pa::decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
                          context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
                          partition_tokens, workspace, workspace_bytes, dtype, stream, &cas);
+}
+
+// ---------------------------------------------------------------------------
+// The fused step for callers that cannot allocate: the split-context partials
+// live in this file-scope array (one copy per GPU, held until the process
+// ends).  Host code never passes the array's name to a kernel: it is a host
+// stand-in, not a device address.  The address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+namespace pa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_decode_step_noalloc(void* out, const void* query, const void* key,
+                                      const void* value, void* key_cache, void* value_cache,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+                                      int32_t NB, int32_t MB, int32_t max_context_len,
+                                      float scale, int32_t partition_tokens, int32_t dtype,
+                                      void* stream) {
+  if (bs < 1 || MB < 1 || max_context_len < 1) return PA_ERR_INVALID;
+  const int32_t eff_ctx = static_cast<int32_t>(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(MB) * bs));
+  const size_t need = pa_decode_workspace_bytes(S, Hq, D, eff_ctx, partition_tokens);
+  if (need > PA_STATIC_SCRATCH_BYTES) return PA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = pa::scratch_on_current_device(&ws);
+    if (rc != PA_OK) return rc;
+  }
+  return pa_decode_step(out, query, key, value, key_cache, value_cache, block_tables,
+                        context_lens, S, Hq, Hkv, D, bs, NB, MB, max_context_len, scale,
+                        partition_tokens, ws, need > 0 ? PA_STATIC_SCRATCH_BYTES : 0, dtype,
+                        stream);
 }

@@ -39,7 +39,7 @@ def test_one_hip_runtime_mapped():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert pa.status_string(code) not in ("", "unknown status")
     assert pa.status_string(7) == "unknown status"
 
@@ -220,3 +220,13 @@ def test_binding_refuses_host_tensors():
         pa.pa_reshape_and_cache(torch.zeros(1, 2, 64, dtype=torch.float16),
                                 torch.zeros(1, 2, 64, dtype=torch.float16), kc, kc.clone(),
                                 torch.zeros(1, dtype=torch.int64))
+
+
+def test_noalloc_step_refuses_more_than_the_static_scratch():
+    # the size check comes before any HIP call, so this runs without a GPU
+    need = pa.lib().pa_decode_workspace_bytes(64, 64, 128, 65536, 16)
+    assert need > pa.PA_STATIC_SCRATCH_BYTES
+    rc = pa.lib().pa_decode_step_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 8,
+                                         128, 16, 100, 4096, 65536, 0.1, 16, pa.PA_BF16, None)
+    assert rc == pa.PA_ERR_TOO_LARGE
+    assert "static scratch" in pa.status_string(rc)
