@@ -9,16 +9,24 @@ timed beside it.
 Inputs are seeded synthetic data already resident in HBM; slots and block
 tables come from the library's host allocator before the timed region.
 
-Default workload: LLaMA-13B-shaped decode layer, 128 sequences, 40 heads of
-128, bfloat16 KV, block size 16, context lengths lognormal (median 700,
-sigma 0.5, at most 2048).  ``value`` is algorithmic KV bytes (every attended
-token's K and V row once per head) per second of whole step.  The
-``roofline`` object prices the decode kernel alone against the 8 TB/s HBM
-peak; ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of
-the same workload.
+Default run (no --workload): a launcher that makes no GPU call itself and
+runs every measurement in a child process of its own, one after another:
+  * the headline, the LLaMA-13B-shaped decode layer (128 sequences, 40 heads
+    of 128, bfloat16 KV, block size 16, context lengths lognormal with median
+    700, sigma 0.5, at most 2048), with the read-bandwidth probes and the CPU
+    oracle baseline;
+  * the block-size sweep of that batch (8, 32, 64, 128), one process each;
+  * every other workload (tiny, LLaMA-7B-shaped, shared-prefix parallel
+    sampling at 504- and 512-token prompts, long-context grouped-query), each
+    with its own oracle baseline.
+One JSON line merges them: the headline's fields at the top level, the sweep
+under ``sweep``, the others under ``configs``.  ``value`` is algorithmic KV
+bytes (every attended token's K and V row once per head) per second of whole
+step; ``roofline`` prices the decode kernel against the 8 TB/s HBM peak;
+``cpu_baseline`` times the float64 CPU oracle on the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--bs 16] [--partition P]
-                    [--no-sweep] [--no-cpu-baseline] [--calibrate-copy]
+    python bench.py [--steps K] [--warmup W] [--bs 16] [--no-sweep]
+    python bench.py --workload NAME [...]   # one workload, in this process
 """
 from __future__ import annotations
 
@@ -26,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -36,6 +45,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_llama13b_bs16.json")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_198_amd", "csrc", f)
                for f in ("pa_decode.hip", "pa_device.h")]
+WORKLOADS = ["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix", "system_prompt", "beam",
+             "prefill"]
 
 
 def decode_source_sha() -> str:
@@ -52,10 +63,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama13b",
-                    choices=["llama13b", "llama7b", "long_gqa", "tiny", "shared_prefix",
-                             "system_prompt", "beam", "prefill"],
-                    help="decode workload to time (default: the 13B-shaped batch)")
+    ap.add_argument("--workload", default=None, choices=WORKLOADS,
+                    help="time this workload in this process (default: run the headline, the "
+                         "block-size sweep and the other workloads, each in a child process)")
     ap.add_argument("--bs", type=int, default=16)
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition tokens (0 = single pass, -1 = library default for the shape)")
@@ -66,8 +76,11 @@ def parse():
     ap.add_argument("--prefix-tokens", type=int, default=0,
                     help="shared_prefix / system_prompt: tokens per shared-prefix work item "
                          "(0 = whole prefix)")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="default run: skip the block-size sweep and the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle work per workload for the CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the plain HBM probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -146,8 +159,7 @@ class Step:
 
 def kernel_name(st) -> str:
     w = st.w
-    mfma = (w.dtype in ("bf16", "f16") and w.D == 128 and w.Hq // w.Hkv == 8
-            and st.part % 32 == 0)
+    mfma = w.dtype in ("bf16", "f16") and w.D == 128 and w.Hq // w.Hkv == 8
     k = "pa::decode_gqa_mfma_kernel" if mfma else "pa::decode_kernel"
     parts = -(-st.max_ctx // st.part) if st.part else 1
     red = "" if parts < 2 else (" + reduce_wide_kernel" if parts >= 16 else " + reduce_kernel")
@@ -178,46 +190,136 @@ def traffic_bytes():
     return float(t["bytes_per_launch"])
 
 
-def cpu_baseline(step, budget_s=10.0):
-    """The float64 oracle on the host, on the first sequences of the same
-    workload until about ``budget_s`` seconds of work."""
+def host_threads():
+    """(host cores this process may run on, BLAS threads numpy uses)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = 1
+    return cores, int(blas)
+
+
+def timed_reps(fn, budget_s, max_reps=5):
+    """Run ``fn`` (returns its own seconds) at least once and until about
+    ``budget_s`` seconds are spent; the median and the count."""
+    times = [fn()]
+    while sum(times) < budget_s and len(times) < max_reps:
+        times.append(fn())
+    return float(np.median(times)), len(times)
+
+
+def baseline_record(kv_bytes, secs, reps, what):
+    cores, blas = host_threads()
+    return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
+            "s_per_step": secs, "reps": reps, "host_cores": cores, "blas_threads": blas,
+            "sample": what + "; float64 numpy (gathers single-threaded, matrix-vector "
+                             f"products through BLAS with up to {blas} threads)"}
+
+
+def cpu_baseline(step, budget_s=8.0):
+    """The float64 oracle on the host over the same decode step: the cache
+    write of every sequence's new token (slots from the oracle's own walk of
+    the block tables) and the attention of every sequence, on host copies of
+    the blocks the batch references.  One whole step, repeated for about
+    ``budget_s`` seconds; the first sequences only when one step would take
+    far longer than that (the record says how many)."""
     import oracle.decode as od
     from paged_kv_cache_198_amd import synth
     torch = step.torch
     w = step.w
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
 
-    def run(seqs):
+    def host_inputs(seqs):
         need = [-(-int(w.context_lens[s]) // w.bs) for s in seqs]
         blocks = np.unique(np.concatenate([w.block_tables[s, :n] for s, n in zip(seqs, need)]))
         remap = np.full(w.NB, -1, dtype=np.int64)
         remap[blocks] = np.arange(len(blocks))
-        idx = torch.from_numpy(blocks.astype(np.int64)).cuda()
-        kc = synth.to_numpy_storage(w.key_cache.index_select(0, idx))
-        vc = synth.to_numpy_storage(w.value_cache.index_select(0, idx))
-        tab = np.where(w.block_tables[seqs] >= 0, remap[np.maximum(w.block_tables[seqs], 0)], -1)
-        q = synth.to_numpy_storage(w.q[seqs])
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(w.q.device)
+        sel = torch.tensor(seqs, device=w.q.device)
+        return dict(
+            kc=synth.to_numpy_storage(w.key_cache.index_select(0, idx)),
+            vc=synth.to_numpy_storage(w.value_cache.index_select(0, idx)),
+            tab=np.where(w.block_tables[seqs] >= 0,
+                         remap[np.maximum(w.block_tables[seqs], 0)], -1),
+            lens=w.context_lens[seqs], q=synth.to_numpy_storage(w.q.index_select(0, sel)),
+            nk=synth.to_numpy_storage(w.new_key.index_select(0, sel)),
+            nv=synth.to_numpy_storage(w.new_value.index_select(0, sel)))
+
+    def run(h):
         t0 = time.perf_counter()
-        od.paged_decode(q, kc, vc, tab, w.context_lens[seqs], w.scale, w.dtype)
+        slots = [od.slot_of(h["tab"][i], int(h["lens"][i]) - 1, w.bs) for i in range(len(h["lens"]))]
+        od.reshape_and_cache(h["nk"], h["nv"], h["kc"], h["vc"], slots, inplace=True)
+        od.paged_decode(h["q"], h["kc"], h["vc"], h["tab"], h["lens"], w.scale, w.dtype)
         return time.perf_counter() - t0
 
-    probe = run([0])
-    per_seq = max(probe, 1e-3)
-    n = int(min(w.S, max(1, budget_s / per_seq)))
-    seqs = list(range(n))
+    few = list(range(min(8, w.S)))
+    hf = host_inputs(few)
+    per_tok = min(run(hf), run(hf)) / max(int(np.sum(w.context_lens[few])), 1)
+    est = per_tok * float(np.sum(w.context_lens))
+    if est <= 4 * budget_s:
+        seqs = list(range(w.S))
+        what = f"one whole decode step ({w.S} sequences)"
+    else:
+        csum = np.cumsum(w.context_lens.astype(np.int64))
+        n = int(max(1, np.searchsorted(csum, budget_s / per_tok)))
+        seqs = list(range(min(n, w.S)))
+        what = (f"the first {len(seqs)} of {w.S} sequences of one decode step (a whole step "
+                f"would take about {est:.0f} s); value scaled by their KV bytes")
+    h = host_inputs(seqs)
     kv = int(np.sum(w.context_lens[seqs].astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
-    secs, reps = 0.0, 0
-    while reps == 0 or (secs < budget_s and reps < 50):
-        secs += run(seqs)
-        reps += 1
-    return {"value": kv * reps / secs / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {n} of {w.S} sequences ({kv / 1e9:.3f} GB of KV) x {reps} "
-                      f"passes, {secs:.1f} s, float64 numpy"}
+    secs, reps = timed_reps(lambda: run(h), budget_s)
+    return baseline_record(kv, secs, reps, f"{what}, median of {reps}")
+
+
+def cpu_baseline_shared_prefix(sc, budget_s=8.0):
+    """The oracle's own drive of the parallel-sampling script (its
+    allocator, copy-on-write copies and cache writes, untimed) up to the
+    decode step, then that step timed once: every sample's next slot and
+    copy-on-write copies, the cache write of the new tokens and the attention
+    of all samples."""
+    import oracle.alloc as oa
+    import oracle.decode as od
+    from paged_kv_cache_198_amd import synth
+    kc = synth.to_numpy_storage(sc.key_cache).copy()
+    vc = synth.to_numpy_storage(sc.value_cache).copy()
+    pk, pv = synth.to_numpy_storage(sc.prompt_k), synth.to_numpy_storage(sc.prompt_v)
+    tk, tv = synth.to_numpy_storage(sc.tail_k), synth.to_numpy_storage(sc.tail_v)
+    sk, sv = synth.to_numpy_storage(sc.step_k), synth.to_numpy_storage(sc.step_v)
+    q = synth.to_numpy_storage(sc.q)
+    alloc = oa.Allocator(sc.NB, sc.bs, init_order=sc.init_order)
+    for i in range(sc.prompts):
+        sid = sc.seq_id(i, 0)
+        alloc.create(sid)
+        slots = [alloc.append(sid)[0] for _ in range(sc.prompt_len)]
+        od.reshape_and_cache(pk[i], pv[i], kc, vc, slots, inplace=True)
+        for j in range(1, sc.samples):
+            alloc.fork(sid, sc.seq_id(i, j))
+
+    def advance(who, k, v):
+        pairs, slots = [], []
+        for s in who:
+            slot, src, dst = alloc.append(s)
+            slots.append(slot)
+            if src >= 0:
+                pairs.append((src, dst))
+        od.copy_blocks([kc], [vc], pairs, inplace=True)
+        od.reshape_and_cache(k, v, kc, vc, slots, inplace=True)
+
+    for t in range(int(sc.tails.max()) if sc.S else 0):
+        who = [s for s in range(sc.S) if t < sc.tails[s]]
+        advance(who, tk[who, t], tv[who, t])
+    seqs = list(range(sc.S))
+    t0 = time.perf_counter()
+    advance(seqs, sk, sv)
+    MB = max(-(-alloc.seq_len(s) // sc.bs) for s in seqs)
+    tables, lens = alloc.build_batch(seqs, MB)
+    od.paged_decode(q, kc, vc, np.array(tables), np.array(lens), sc.scale, sc.dtype)
+    secs = time.perf_counter() - t0
+    kv = int(np.sum(np.asarray(lens, dtype=np.int64))) * 2 * sc.Hkv * sc.D * synth.ELEM_BYTES[sc.dtype]
+    return baseline_record(kv, secs, 1, f"one whole decode step ({sc.S} samples, logical bytes: "
+                                        "each sample's whole context), the state built by the "
+                                        "oracle's own allocator and cache writes beforehand")
 
 
 def read_probe(pa, torch, nbytes, grids, reps=10):
@@ -375,7 +477,8 @@ def run_shared_prefix(args, pa, synth, torch):
                      "note": "achieved counts the bytes the cascade must read: each shared "
                              "prefix once per group, every suffix once"},
         "plain_fused_step": {"us": plain_ms * 1e3, "logical_GBs": gbs(logical, plain_ms),
-                             "speedup_of_cascade": plain_ms / step_ms},
+                             "speedup_of_cascade": plain_ms / step_ms,
+                             "kernel": "pa::decode_kernel (pa_decode_step, fused cache write)"},
         "plan": {"items": plan.n_items, "slots_max": plan.slots_max,
                  "prefix_rows": plan.prefix_rows, "saved_rows": plan.saved_rows,
                  "host_plan_us": plan_us},
@@ -386,6 +489,9 @@ def run_shared_prefix(args, pa, synth, torch):
     }
     if args.workload == "system_prompt":
         return res
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_shared_prefix(sc, args.cpu_budget)
 
     # copy-on-write block copies across the layers of a 40-layer model: the
     # fork-time divergence of this batch (one pair per sample that writes
@@ -657,71 +763,31 @@ def run_beam(args, pa, synth, torch):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "single-GPU benchmark: the decode path is not sharded over GPUs; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import torch
-    import paged_kv_cache_198_amd as pa
-    from paged_kv_cache_198_amd import synth
-
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    pa.lib()
-    if args.workload == "prefill":
-        print("[bench] prefill", file=sys.stderr, flush=True)
-        print(json.dumps(run_prefill(args, pa, synth, torch)), flush=True)
-        return
-    if args.workload == "beam":
-        print("[bench] beam search", file=sys.stderr, flush=True)
-        print(json.dumps(run_beam(args, pa, synth, torch)), flush=True)
-        return
-    if args.workload in ("shared_prefix", "system_prompt"):
-        print(f"[bench] building {args.workload} state", file=sys.stderr, flush=True)
-        print(json.dumps(run_shared_prefix(args, pa, synth, torch)), flush=True)
-        return
-    print(f"[bench] building workload {args.workload} bs={args.bs}", file=sys.stderr, flush=True)
-    st = Step(pa, synth, torch, args.bs, args.seed, args.partition, args.workload)
+def run_decode(args, pa, synth, torch):
+    """One decode workload in this process: the fused step, the two-call
+    step, optionally the read probes and the oracle baseline."""
+    workload = args.workload or "llama13b"
+    print(f"[bench] building workload {workload} bs={args.bs}", file=sys.stderr, flush=True)
+    st = Step(pa, synth, torch, args.bs, args.seed, args.partition, workload)
     w = st.w
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
     step_ms, wall = st.run(args.steps, args.warmup, fused=True)
     un_step_ms, _ = st.run(max(20, args.steps // 4), args.warmup, fused=False)
-
-    sweep = {}
-    if not args.no_sweep and args.workload == "llama13b":
-        for bs in (8, 16, 32, 64, 128):
-            if bs == args.bs:
-                continue
-            print(f"[bench] sweep bs={bs}", file=sys.stderr, flush=True)
-            other = Step(pa, synth, torch, bs, args.seed, args.partition)
-            s_ms, _ = other.run(max(20, args.steps // 4), args.warmup, fused=True)
-            lens_h = other.lens.cpu().numpy().astype(np.int64)
-            blocks = (lens_h + bs - 1) // bs
-            # closed form: with residues spread evenly, a sequence's last
-            # block leaves (bs - 1) / 2 slots empty on average
-            mod_w = len(lens_h) * (bs - 1) / 2
-            sweep[f"bs{bs}"] = {"us_per_step": s_ms * 1e3,
-                                "tail_waste": float((blocks * bs - lens_h).sum()
-                                                    / (blocks * bs).sum()),
-                                "tail_waste_model": float(mod_w / (lens_h.sum() + mod_w)),
-                                "GBs": other.kv_bytes / (s_ms * 1e-3) / 1e9,
-                                "frac_hbm_peak": other.kv_bytes / (s_ms * 1e-3) / 1e9
-                                / HBM_PEAK_GBS}
-            del other
-            torch.cuda.empty_cache()
-
+    lens_h = st.lens.cpu().numpy().astype(np.int64)
+    blocks = (lens_h + w.bs - 1) // w.bs
+    # closed form: with residues spread evenly, a sequence's last block
+    # leaves (bs - 1) / 2 slots empty on average
+    mod_w = len(lens_h) * (w.bs - 1) / 2
     # The step is one launch of the fused kernel (plus the reduce pass when
     # partitioned); its average launch duration, gaps included, is the step
     # time measured above.
     achieved = st.kv_bytes / (step_ms * 1e-3) / 1e9
+    headline = workload == "llama13b"
     line = {
         "metric": "decode-attention KV GB/s (frac of MI355X HBM peak) + us/step, "
-                  "13B-shaped batch",
-        "value": st.kv_bytes / (step_ms * 1e-3) / 1e9,
+                  + ("13B-shaped batch" if headline else f"{workload} batch"),
+        "value": achieved,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -732,27 +798,31 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) q/K/V, lognormal context lengths)",
+        "data": "synthetic (seeded N(0,1) q/K/V, " + (
+            "lognormal" if synth.CONFIGS[workload]["lengths"][0] == "lognormal" else "uniform")
+            + " context lengths)",
         "config": {
-            "workload": describe(args.workload, w),
+            "workload": describe(workload, w),
             "S": w.S, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "block_size": w.bs,
             "tokens": int(np.sum(w.context_lens)), "kv_bytes": st.kv_bytes,
             "partition_tokens": st.part, "seed": args.seed,
         },
-        "frac_hbm_peak_step": st.kv_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "frac_hbm_peak_step": achieved / HBM_PEAK_GBS,
         "two_call_step": {"us_per_step": un_step_ms * 1e3,
+                          "GBs": st.kv_bytes / (un_step_ms * 1e-3) / 1e9,
                           "note": "pa_reshape_and_cache + pa_decode_attention as two launches"},
+        "tail_waste": float((blocks * w.bs - lens_h).sum() / (blocks * w.bs).sum()),
+        "tail_waste_model": float(mod_w / (lens_h.sum() + mod_w)),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_bytes() if (args.workload == "llama13b" and args.bs == 16) else None,
+            "traffic": traffic_bytes() if (headline and args.bs == 16) else None,
             "kernel": kernel_name(st),
             "algorithmic_bytes_per_launch": st.kv_bytes,
         },
-        "sweep": sweep,
         "wall_s_timed": wall,
     }
     if not args.no_probe:
@@ -775,10 +845,142 @@ def main():
         calibrate_copy(torch)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(st)
+        line["cpu_baseline"] = cpu_baseline(st, args.cpu_budget)
     else:
         line["cpu_baseline"] = None
+    return line
+
+
+# The default run's children: (key, arguments).  The headline comes first;
+# the block-size sweep and the other workloads follow, one process each, so
+# no measurement runs in a process that already holds another workload's
+# device memory.
+SWEEP_BS = (8, 16, 32, 64, 128)
+CONFIG_RUNS = [
+    ("tiny", ["--workload", "tiny", "--no-probe"]),
+    ("llama7b", ["--workload", "llama7b", "--no-probe"]),
+    ("shared_prefix_504", ["--workload", "shared_prefix", "--prompt-len", "504"]),
+    ("shared_prefix_512", ["--workload", "shared_prefix", "--prompt-len", "512"]),
+    ("long_gqa", ["--workload", "long_gqa", "--no-probe"]),
+]
+
+
+def decode_summary(r):
+    """The per-workload record kept under ``configs`` / ``sweep``."""
+    out = {"workload": r["config"]["workload"], "dtype": r["dtype"],
+           "us_per_step": r["us_per_step"], "GBs": r["value"],
+           "frac_hbm_peak": r["roofline"]["frac"], "kernel": r["roofline"]["kernel"],
+           "kv_bytes": r["config"]["kv_bytes"],
+           "partition_tokens": r["config"]["partition_tokens"],
+           "two_call_us_per_step": r["two_call_step"]["us_per_step"],
+           "tail_waste": r["tail_waste"], "tail_waste_model": r["tail_waste_model"]}
+    if r.get("cpu_baseline") is not None:
+        out["cpu_baseline"] = r["cpu_baseline"]
+    return out
+
+
+def shared_summary(r):
+    c = r["config"]
+    return {"workload": c["workload"], "dtype": r["dtype"],
+            "plain": {"us_per_step": r["plain_fused_step"]["us"],
+                      "logical_GBs": r["plain_fused_step"]["logical_GBs"],
+                      "kernel": r["plain_fused_step"]["kernel"]},
+            "cascade": {"us_per_step": r["us_per_step"], "logical_GBs": r["value"],
+                        "read_GBs": r["roofline"]["achieved"],
+                        "frac_hbm_peak_read": r["roofline"]["frac"],
+                        "kernel": "pa::decode_gqa_mfma_kernel over work items + reduce_kernel "
+                                  "(pa_decode_cascade, fused cache write)"},
+            "kv_bytes": {"logical": c["logical_kv_bytes"], "read_by_cascade": c["cascade_kv_bytes"],
+                         "unique": c["unique_kv_bytes"]},
+            "sharing": r["sharing"], "cow_copy": r.get("cow_copy"),
+            "cpu_baseline": r["cpu_baseline"]}
+
+
+def launcher(args):
+    """The default run.  This process never touches the GPU: every
+    measurement runs in a child process, one after another.  A child that
+    fails stops the run (nothing more is started), and the line printed so
+    far carries the error."""
+    base = [sys.executable, os.path.abspath(__file__), "--steps", str(args.steps),
+            "--warmup", str(args.warmup), "--seed", str(args.seed),
+            "--cpu-budget", str(args.cpu_budget)]
+    if args.no_cpu_baseline:
+        base.append("--no-cpu-baseline")
+
+    def child(extra):
+        print(f"[bench] child: {' '.join(extra)}", file=sys.stderr, flush=True)
+        try:
+            r = subprocess.run(base + extra, stdout=subprocess.PIPE, text=True, timeout=300)
+        except subprocess.TimeoutExpired:
+            return None, f"child {' '.join(extra)} ran past 300 s and was stopped"
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            return None, f"child {' '.join(extra)} exited with {r.returncode}"
+        return json.loads(lines[-1]), None
+
+    extra = ["--workload", "llama13b", "--bs", str(args.bs)]
+    if args.no_probe:
+        extra.append("--no-probe")
+    if args.calibrate_copy:
+        extra.append("--calibrate-copy")
+    line, err = child(extra)
+    if err:
+        print(json.dumps({"error": err}), flush=True)
+        sys.exit(1)
+    for k in ("tail_waste", "tail_waste_model"):
+        line.pop(k, None)
+    line["sweep"], line["configs"] = {}, {}
+    if not args.no_sweep:
+        runs = [(f"bs{bs}", ["--workload", "llama13b", "--bs", str(bs), "--no-probe",
+                             "--no-cpu-baseline"]) for bs in SWEEP_BS if bs != args.bs]
+        runs += CONFIG_RUNS
+        for key, extra in runs:
+            r, err = child(extra)
+            if err:
+                line["error"] = err
+                print(json.dumps(line), flush=True)
+                sys.exit(1)
+            if key.startswith("bs"):
+                line["sweep"][key] = decode_summary(r)
+            elif key.startswith("shared_prefix"):
+                line["configs"][key] = shared_summary(r)
+            else:
+                line["configs"][key] = decode_summary(r)
+        line["sweep"]["note"] = ("each block size in a process of its own, after the "
+                                 f"headline (bs {args.bs})")
     print(json.dumps(line), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU benchmark: the decode path is not sharded over GPUs; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.workload is None:
+        launcher(args)
+        return
+    import torch
+    import paged_kv_cache_198_amd as pa
+    from paged_kv_cache_198_amd import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pa.lib()
+    if args.workload == "prefill":
+        print("[bench] prefill", file=sys.stderr, flush=True)
+        print(json.dumps(run_prefill(args, pa, synth, torch)), flush=True)
+        return
+    if args.workload == "beam":
+        print("[bench] beam search", file=sys.stderr, flush=True)
+        print(json.dumps(run_beam(args, pa, synth, torch)), flush=True)
+        return
+    if args.workload in ("shared_prefix", "system_prompt"):
+        print(f"[bench] building {args.workload} state", file=sys.stderr, flush=True)
+        print(json.dumps(run_shared_prefix(args, pa, synth, torch)), flush=True)
+        return
+    print(json.dumps(run_decode(args, pa, synth, torch)), flush=True)
 
 
 if __name__ == "__main__":

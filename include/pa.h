@@ -120,9 +120,9 @@ int pa_reshape_and_cache(const void* key, const void* value,
  *                    256-byte aligned; may be NULL when that size is 0.
  * Supported: dtype any; D in {64, 128}; bs in {8, 16, 32, 64, 128};
  *            Hq / Hkv in {1, 2, 4, 8}.  Grouped heads with Hq / Hkv = 8,
- *            D = 128, f16 / bf16 and partition_tokens a multiple of 32 (or
- *            0) run both products on the matrix cores; every other shape
- *            runs on the vector ALUs. */
+ *            D = 128 and f16 / bf16 run both products on the matrix cores
+ *            (any partition size); every other shape runs on the vector
+ *            ALUs. */
 size_t pa_decode_workspace_bytes(int32_t S, int32_t Hq, int32_t D,
                                  int32_t max_context_len, int32_t partition_tokens);
 

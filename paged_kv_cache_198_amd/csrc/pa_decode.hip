@@ -611,8 +611,7 @@ int decode_impl(void* out, const void* query, const void* new_key, const void* n
   hipStream_t st = static_cast<hipStream_t>(stream);
   // Grouped heads that fill a matrix-core tile go to the MFMA kernel; every
   // other shape runs the vector-ALU kernel.
-  const bool mfma = (dtype == PA_BF16 || dtype == PA_F16) && D == 128 && G == 8 &&
-                    a.part_tokens % 32 == 0;
+  const bool mfma = (dtype == PA_BF16 || dtype == PA_F16) && D == 128 && G == 8;
   int rc;
   if (cas) {
     rc = pa::launch_items_mfma(a, dtype, bs, st);

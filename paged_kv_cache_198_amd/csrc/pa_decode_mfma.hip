@@ -85,8 +85,9 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
   constexpr int NC = GROUP ? 16 : kMG;     // columns that produce output
-  // A tile spans 32/bs blocks when bs divides 32, else it sits inside one
-  // block at offset t0 % bs (a multiple of 32).
+  // A tile spans 16/bs blocks when bs divides 16 (t0 is then a multiple of
+  // bs: partitions are multiples of bs), else it sits inside one block at
+  // offset t0 % bs (a multiple of 16).
   constexpr int NBK = BS >= kMTile ? 1 : kMTile / BS;
   static_assert((kMTile % BS == 0 || BS % kMTile == 0) && BS >= 4, "block size");
   using Tile = TileRegs<NBK>;

@@ -16,3 +16,20 @@ def test_more_than_one_gpu_is_refused():
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2
     assert "--gpus must be 1" in line["error"]
+
+
+def test_default_run_is_a_launcher_that_never_imports_torch(tmp_path):
+    # a torch that cannot be imported: the launcher must still run and
+    # report its first child's failure as a JSON line (the child, which does
+    # import torch, fails)
+    fake = tmp_path / "torch"
+    fake.mkdir()
+    (fake / "__init__.py").write_text("raise ImportError('no torch in the launcher')\n")
+    env = dict(os.environ, PYTHONPATH=str(tmp_path))
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "1",
+                        "--warmup", "0", "--no-sweep"],
+                       capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 1
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["error"].startswith("child --workload llama13b --bs 16")
+    assert "[bench] child: --workload llama13b" in r.stderr

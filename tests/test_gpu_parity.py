@@ -499,15 +499,27 @@ def test_shared_prefix(prompt_len, full):
 
 # ---------------------------------------------------------------------------
 # grouped heads on the matrix cores (G = 8, D = 128, bf16 / f16): block sizes,
-# partitions (multiples of 32 take the MFMA kernel, others the vector-ALU one)
+# partitions (every multiple of bs takes the MFMA kernel)
 # and lengths around tile, block and partition edges
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,bs,part", [("bf16", 8, 512), ("bf16", 32, 0), ("f16", 16, 512),
                                            ("f16", 16, 0), ("bf16", 16, 96), ("bf16", 16, 48),
-                                           ("f16", 8, 64)])
+                                           ("f16", 8, 64), ("bf16", 8, 24), ("f16", 16, 80),
+                                           ("bf16", 32, 96), ("f16", 64, 192), ("bf16", 8, 40)])
 def test_gqa_matrix_core(dtype, bs, part):
+    # every partition size (a multiple of bs) takes the matrix-core kernel
     w = synth.make_decode("long_gqa", device=DEV, S=4, NB=2048, bs=bs, dtype=dtype,
                           lengths=("uniform", 1, 3000))
+    check_decode(w, part=part)
+
+
+@pytest.mark.parametrize("dtype,D,part", [("f32", 128, 0), ("f32", 128, 48), ("bf16", 64, 96),
+                                          ("f16", 64, 0)])
+def test_grouped_eight_vector_alu(dtype, D, part):
+    # G = 8 outside the matrix-core set (float32, or D = 64) runs on the
+    # vector ALUs
+    w = synth.make_decode("long_gqa", device=DEV, S=4, NB=2048, dtype=dtype, D=D,
+                          lengths=("uniform", 1, 2000))
     check_decode(w, part=part)
 
 
@@ -756,6 +768,7 @@ def test_cascade_step(G, Hkv, bs, dtype, part, pfx):
     ("long_gqa", dict(S=3, NB=1024, lengths=("uniform", 700, 4000)), 512),
     ("long_gqa", dict(S=4, NB=1024, lengths=("fixed", [1, 31, 32, 1025])), 0),
     ("long_gqa", dict(S=3, NB=2048, bs=8, dtype="f16", lengths=("uniform", 1, 3000)), 64),
+    ("long_gqa", dict(S=3, NB=2048, lengths=("uniform", 1, 3000)), 48),
 ])
 def test_cascade_without_sharing(name, over, part):
     # no shared blocks: every item is one sequence's partition; the cache
@@ -771,7 +784,7 @@ def test_cascade_without_sharing(name, over, part):
     err = float(np.max(np.abs(widened(out2, w.dtype) - ref)))
     note(f"  max abs err {err:.3e}")
     assert err <= TOL[w.dtype]
-    if w.Hq // w.Hkv == 8 and part % 32 == 0:
+    if w.Hq // w.Hkv == 8:
         assert torch.equal(bits(out1), bits(out2))
 
 
