@@ -24,8 +24,11 @@
 // leaves the full dot product in every lane of the row.
 //
 // A wavefront's token rows never straddle a block, so the block-table entry
-// of each row group is wave-uniform: it is read with a scalar load and folded
-// into the scalar base of the vector loads.  K/V rows go straight from HBM to
+// of each row group is wave-uniform.  The fused step's store in the loop
+// could alias the table as far as the compiler knows, so it reads each entry
+// with a vector load and waits for it before the tile's K/V loads; that
+// paces each wavefront's requests, and measured faster than scalar reads of
+// all of a tile's entries at once.  K/V rows go straight from HBM to
 // registers (each byte is consumed by exactly one lane, so an LDS hop would
 // add traffic without reuse).  Tiles wholly inside the context load without
 // predication; in the last tile, tokens past the context are never loaded
@@ -103,8 +106,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 
   // Row group j of a tile starting at t0 holds tokens t0 + j*RPW + [0, RPW):
   // t0 is a multiple of RPW and RPW divides bs, so those RPW tokens share one
-  // block and the block number is the same for the whole wavefront.  It is
-  // read with a scalar load and folded into the scalar base address; the only
+  // block and the block number is the same for the whole wavefront; the only
   // per-lane address term is the lane's row and 16-byte column.
   const int32_t* trow = a.block_tables + static_cast<size_t>(s) * a.MB;
   const size_t bstride = static_cast<size_t>(a.Hkv) * BS * D * EB;  // bytes per block
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // merge the waves; one thread per (head, element)
   for (int i = tid; i < G * D; i += kWaves * 64) {

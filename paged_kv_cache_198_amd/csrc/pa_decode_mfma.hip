@@ -52,7 +52,12 @@ namespace pa {
 
 namespace {
 
-constexpr int kMWaves = 2;                 // wavefronts per workgroup
+// Wavefronts per workgroup and register stages: plain grouped-query decode
+// runs 2 and 1, work items 2 and 2.  (One wavefront with two stages per
+// 512-token partition, 149 VGPRs, fits the long-context grid into the
+// resident slots in one round and runs as fast as two with one stage.)
+constexpr int kPlainWaves = 2, kPlainStages = 1;
+constexpr int kItemWaves = 2, kItemStages = 2;
 constexpr int kMTile = 16;                 // tokens per wavefront per tile
 constexpr int kMD = 128;                   // head dim
 constexpr int kMG = 8;                     // query heads per KV head
@@ -79,8 +84,8 @@ struct TileRegs {
 // tables share the item's token range, which is read once for all of them;
 // a suffix item has one member, the sequence itself.  Each column writes a
 // partial to its member's workspace slot, or, for slot -1, the final output.
-template <int DT, int BS, bool GROUP>
-__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(GROUP ? 3 : 4)))
+template <int DT, int BS, bool GROUP, int kMWaves, int kStages>
+__global__ __launch_bounds__(kMWaves * 64) __attribute__((amdgpu_waves_per_eu(kStages == 2 ? 3 : 4)))
 void decode_gqa_mfma_kernel(DecodeArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
@@ -346,7 +351,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   // The loads are issued without conditions (a tile past the end loads zeros
   // without touching memory), so the compiler can count the loads in flight
   // on every path and wait only for the ones each use needs.
-  if constexpr (!GROUP) {
+  if constexpr (kStages == 1) {
     // One register stage: the next tile's loads go into the registers the
     // current tile has just left for LDS, and are in flight while it is
     // used.  About 125 VGPRs: 4 wavefronts per SIMD.
@@ -401,7 +406,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<uint4*>(const_cast<char*>(vb) + dst) = nv;
     }
   }
-  __syncthreads();                         // every wavefront is done with its tile
+  lds_barrier();                           // every wavefront is done with its tile
 
   // column n's sum over the four lane groups
   l_run += __shfl_xor(l_run, 16);
@@ -416,7 +421,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
       red.l[w][n] = l_run;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   for (int i = tid; i < NC * kMD; i += kMWaves * 64) {
     const int gi = i / kMD;
@@ -462,7 +467,8 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int DT, bool GROUP>
+template <int DT, bool GROUP, int NW = GROUP ? kItemWaves : kPlainWaves,
+          int NST = GROUP ? kItemStages : kPlainStages>
 int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
   // Plain decode: grid (KV head, partition, sequence), so a sequence's
   // partitions are dispatched together (3-4% faster on the long-context
@@ -470,13 +476,13 @@ int launch_bs(const DecodeArgs& a, int32_t bs, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(a.Hkv),
                   static_cast<uint32_t>(GROUP ? a.n_items : a.grid_parts),
                   static_cast<uint32_t>(GROUP ? 1 : a.S));
-  const dim3 block(kMWaves * 64);
+  const dim3 block(NW * 64);
   switch (bs) {
-    case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8, GROUP>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16, GROUP>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32, GROUP>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 64, GROUP>), grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 128, GROUP>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 8, GROUP, NW, NST>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 16, GROUP, NW, NST>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 32, GROUP, NW, NST>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 64, GROUP, NW, NST>), grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL((decode_gqa_mfma_kernel<DT, 128, GROUP, NW, NST>), grid, block, 0, st, a); break;
     default: return PA_ERR_UNSUPPORTED;
   }
   return launch_status();

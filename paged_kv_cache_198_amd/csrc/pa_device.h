@@ -27,6 +27,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #define PA_DECODE_NT 1
 #endif
 
+
+
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // K/V rows are read exactly once: optionally mark the loads non-temporal.
@@ -111,6 +113,17 @@ __device__ __forceinline__ float row_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that orders LDS accesses only.  On this architecture one
+// counter tracks both vector-memory loads and stores, so a full
+// __syncthreads() makes a wavefront wait there until its global stores (the
+// fused step's new row) have completed; this barrier does not, and nothing
+// in the workgroup reads those stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A block-table entry at a wavefront-uniform index, read through the
 // constant address space: the table is never written during a launch, and
 // loads from that space at uniform addresses become scalar loads even after
@@ -145,6 +158,7 @@ struct DecodeArgs {
   // Shared-prefix work items, kItemInts ints each (see pa_cascade_plan).
   const int32_t* items;
   int32_t n_items;
+
   int32_t S, Hq, Hkv, NB, MB, max_ctx;
   int32_t part_tokens;  // 0: one pass over the whole context
   int32_t pmax;         // workspace slots per (sequence, query head)
