@@ -3,7 +3,12 @@
 This module is the one place both sides of a parity check get their inputs
 from.  It draws context lengths, a physical block permutation, block tables
 and N(0,1) query/key/value values; it performs no attention, softmax, slot or
-cache arithmetic.  Everything is a function of ``seed``: integer structure
+cache arithmetic, and hands out no slot: where a test needs slots, the
+library side takes them from its allocator and the oracle side from its own
+walk of the tables.  The one place it reads the tables is ``filled_mask``,
+which decides which pool slots get values and which NaN; a mistake there
+would put NaN where a token should be, and every parity test requires finite
+outputs.  Everything is a function of ``seed``: integer structure
 (lengths, permutation, tables, tails, allocator start order) comes from
 ``numpy.random.default_rng(seed)``, floating-point values from a
 ``torch.Generator`` seeded with the same number on the requested device, drawn
