@@ -4,8 +4,10 @@
 A step is the whole hot path over one batch: the cache write of each
 sequence's new token and paged decode attention over its context.  It is
 timed in both of the library's forms, as two calls (pa_reshape_and_cache,
-then pa_decode_attention) and as the fused pa_decode_step (one launch), and
-quoted on the faster (``step`` names it); the other is reported beside it.
+then pa_decode_attention) and as the fused pa_decode_step (one launch),
+alternating over three rounds of exactly K steps each; each form's median
+is kept and the step is quoted on the faster (``step`` names it), the other
+reported beside it.
 Inputs are seeded synthetic data already resident in HBM; slots and block
 tables come from the library's host allocator before the timed region.
 
@@ -794,8 +796,16 @@ def run_decode(args, pa, synth, torch):
     w = st.w
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
-    two_ms, wall_two = st.run(args.steps, args.warmup, fused=False)
-    fused_ms, wall_fused = st.run(args.steps, args.warmup, fused=True)
+    # The two forms alternate over three rounds (each round: W warm-up
+    # steps, then exactly K timed steps per form) and each form's median is
+    # kept, so neither is always the one timed first after the set-up.
+    runs = {False: [], True: []}
+    for _ in range(3):
+        for fused in (False, True):
+            runs[fused].append(st.run(args.steps, args.warmup, fused=fused))
+    med = lambda rs: sorted(rs)[len(rs) // 2]
+    two_ms, wall_two = med(runs[False])
+    fused_ms, wall_fused = med(runs[True])
     kern_ms = st.kernel_time(args.steps, args.warmup)
     # the step is quoted on whichever form is faster on this workload
     fused_wins = fused_ms < two_ms
@@ -838,9 +848,11 @@ def run_decode(args, pa, synth, torch):
         "step": "fused" if fused_wins else "two_call",
         "two_call_step": {"us_per_step": two_ms * 1e3,
                           "GBs": st.kv_bytes / (two_ms * 1e-3) / 1e9,
+                          "rounds_us": [r[0] * 1e3 for r in runs[False]],
                           "note": "pa_reshape_and_cache + pa_decode_attention as two launches"},
         "fused_step": {"us_per_step": fused_ms * 1e3,
                        "GBs": st.kv_bytes / (fused_ms * 1e-3) / 1e9,
+                       "rounds_us": [r[0] * 1e3 for r in runs[True]],
                        "note": "pa_decode_step: the cache write folded into the attention launch"},
         "tail_waste": float((blocks * w.bs - lens_h).sum() / (blocks * w.bs).sum()),
         "tail_waste_model": float(mod_w / (lens_h.sum() + mod_w)),
