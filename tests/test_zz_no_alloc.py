@@ -104,3 +104,11 @@ def test_noalloc_refuses_more_than_the_scratch():
     assert e.value.status == pa.PA_ERR_TOO_LARGE
     torch.cuda.synchronize()
     assert torch.equal(bits(kc), before)           # nothing was enqueued
+
+
+def test_noalloc_full_long_context_batch():
+    # the largest workload's partials (8 sequences x 64 query heads, contexts
+    # up to 32k tokens in 512-token partitions: 17 MB) fit the static scratch
+    w = synth.make_decode("long_gqa", device=DEV)
+    ref, got = both(w, w.partition_tokens)
+    assert_same(ref, got)
