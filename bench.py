@@ -242,19 +242,44 @@ def baseline_record(kv_bytes, secs, reps, what):
                              f"products through BLAS with up to {blas} threads)"}
 
 
-def cpu_baseline(step, budget_s=8.0):
+class OracleStep:
     """The float64 oracle on the host over the same decode step: the cache
     write of every sequence's new token (slots from the oracle's own walk of
     the block tables) and the attention of every sequence, on host copies of
-    the blocks the batch references.  One whole step, repeated for about
-    ``budget_s`` seconds; the first sequences only when one step would take
-    far longer than that (the record says how many)."""
-    import oracle.decode as od
-    from paged_kv_cache_198_amd import synth
-    torch = step.torch
-    w = step.w
+    the blocks the batch references.
 
-    def host_inputs(seqs):
+    The host inputs are copied when this object is built, before any GPU
+    step touches the pools.  ``time`` repeats one whole step for about
+    ``budget_s`` seconds (the first sequences only when a whole step would
+    take far longer; the record says how many) and compares the oracle's
+    output with the GPU's on the same sequences."""
+
+    def __init__(self, step, budget_s=8.0):
+        import oracle.decode as od
+        self.od = od
+        self.step = step
+        self.budget_s = budget_s
+        w = step.w
+        few = list(range(min(8, w.S)))
+        hf = self._host_inputs(few)
+        per_tok = min(self._run(hf)[0], self._run(self._host_inputs(few))[0]) / max(
+            int(np.sum(w.context_lens[few])), 1)
+        est = per_tok * float(np.sum(w.context_lens))
+        if est <= 4 * budget_s:
+            self.seqs = list(range(w.S))
+            self.what = f"one whole decode step ({w.S} sequences)"
+        else:
+            csum = np.cumsum(w.context_lens.astype(np.int64))
+            n = int(max(1, np.searchsorted(csum, budget_s / per_tok)))
+            self.seqs = list(range(min(n, w.S)))
+            self.what = (f"the first {len(self.seqs)} of {w.S} sequences of one decode step (a "
+                         f"whole step would take about {est:.0f} s); value scaled by their KV bytes")
+        self.h = self._host_inputs(self.seqs)
+
+    def _host_inputs(self, seqs):
+        from paged_kv_cache_198_amd import synth
+        w = self.step.w
+        torch = self.step.torch
         need = [-(-int(w.context_lens[s]) // w.bs) for s in seqs]
         blocks = np.unique(np.concatenate([w.block_tables[s, :n] for s, n in zip(seqs, need)]))
         remap = np.full(w.NB, -1, dtype=np.int64)
@@ -270,30 +295,34 @@ def cpu_baseline(step, budget_s=8.0):
             nk=synth.to_numpy_storage(w.new_key.index_select(0, sel)),
             nv=synth.to_numpy_storage(w.new_value.index_select(0, sel)))
 
-    def run(h):
+    def _run(self, h):
+        od, w = self.od, self.step.w
         t0 = time.perf_counter()
         slots = [od.slot_of(h["tab"][i], int(h["lens"][i]) - 1, w.bs) for i in range(len(h["lens"]))]
         od.reshape_and_cache(h["nk"], h["nv"], h["kc"], h["vc"], slots, inplace=True)
-        od.paged_decode(h["q"], h["kc"], h["vc"], h["tab"], h["lens"], w.scale, w.dtype)
-        return time.perf_counter() - t0
+        out = od.paged_decode(h["q"], h["kc"], h["vc"], h["tab"], h["lens"], w.scale, w.dtype)
+        return time.perf_counter() - t0, out
 
-    few = list(range(min(8, w.S)))
-    hf = host_inputs(few)
-    per_tok = min(run(hf), run(hf)) / max(int(np.sum(w.context_lens[few])), 1)
-    est = per_tok * float(np.sum(w.context_lens))
-    if est <= 4 * budget_s:
-        seqs = list(range(w.S))
-        what = f"one whole decode step ({w.S} sequences)"
-    else:
-        csum = np.cumsum(w.context_lens.astype(np.int64))
-        n = int(max(1, np.searchsorted(csum, budget_s / per_tok)))
-        seqs = list(range(min(n, w.S)))
-        what = (f"the first {len(seqs)} of {w.S} sequences of one decode step (a whole step "
-                f"would take about {est:.0f} s); value scaled by their KV bytes")
-    h = host_inputs(seqs)
-    kv = int(np.sum(w.context_lens[seqs].astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
-    secs, reps = timed_reps(lambda: run(h), budget_s)
-    return baseline_record(kv, secs, reps, f"{what}, median of {reps}")
+    def time(self, gpu_out=None):
+        """The baseline record; ``gpu_out`` is the GPU's output of the same
+        step ([S, Hq, D], any device), compared on the sampled sequences."""
+        from paged_kv_cache_198_amd import synth
+        w = self.step.w
+        kv = int(np.sum(w.context_lens[self.seqs].astype(np.int64))) * 2 * w.Hkv * w.D * w.elem_bytes
+        outs = []
+
+        def once():
+            t, o = self._run(self.h)
+            outs.append(o)
+            return t
+
+        secs, reps = timed_reps(once, self.budget_s)
+        rec = baseline_record(kv, secs, reps, f"{self.what}, median of {reps}")
+        if gpu_out is not None:
+            got = self.od.widen(synth.to_numpy_storage(gpu_out.index_select(
+                0, self.step.torch.tensor(self.seqs, device=gpu_out.device))), w.dtype)
+            rec["max_abs_err_vs_gpu"] = float(np.max(np.abs(got - outs[-1])))
+        return rec
 
 
 def cpu_baseline_shared_prefix(sc, budget_s=8.0):
@@ -794,6 +823,11 @@ def run_decode(args, pa, synth, torch):
     print(f"[bench] building workload {workload} bs={args.bs}", file=sys.stderr, flush=True)
     st = Step(pa, synth, torch, args.bs, args.seed, args.partition, workload)
     w = st.w
+    oracle_step = None
+    if not args.no_cpu_baseline:
+        # the oracle's host inputs, copied before any GPU step writes the pools
+        print("[bench] oracle inputs to the host", file=sys.stderr, flush=True)
+        oracle_step = OracleStep(st, args.cpu_budget)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
     # The two forms alternate over three rounds (each round: W warm-up
@@ -887,9 +921,10 @@ def run_decode(args, pa, synth, torch):
         line["roofline"]["frac_of_read_probe"] = line["roofline"]["achieved"] / max(same.values())
     if args.calibrate_copy:
         calibrate_copy(torch)
-    if not args.no_cpu_baseline:
+    if oracle_step is not None:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(st, args.cpu_budget)
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = oracle_step.time(gpu_out=st.out)
     else:
         line["cpu_baseline"] = None
     return line
