@@ -12,16 +12,22 @@
 // One workgroup of 8 wavefronts per (KV head g, sequence s, query tile),
 // ordered so each XCD runs whole (s, g) pairs (see the kernel's prologue).  A
 // wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
-// KV head g, each column with its own causal limit.  Per 32-token key tile:
-//   * all 512 lanes load 64 keys' K and V rows once (16 bytes each, raw
-//     buffer loads that return zero past a block or the range) into LDS,
-//     where the eight wavefronts share them as two 32-key tiles; the next
-//     64 keys' loads are issued before the current ones are used;
+// KV head g, each column with its own causal limit.  Keys go through LDS in
+// 32-key stages:
+//   * a stage's K and V rows are copied from the pool straight into LDS by
+//     the buffer unit (buffer_load_dwordx4 ... lds: each lane's 16 bytes land
+//     at the lane's own slot of a 1 KB run), without passing through
+//     registers.  kPNBuf stage buffers form a ring, so the loads of the next
+//     kPNBuf - 1 stages are in flight while one is used; each stage costs one
+//     workgroup barrier.  Rows are stored unpadded with their 16-byte chunks
+//     permuted (XOR of the chunk index with a function of the row), which
+//     keeps both LDS read patterns below free of bank conflicts;
 //   * S^T = K . Q^T (2 x 4 v_mfma_f32_16x16x32): A = K rows from LDS, B = the
 //     wavefront's queries in registers; lane l then holds 8 scores of
 //     column l%16;
 //   * causal and validity masks, online softmax per column (lazy rescale as
-//     in the decode kernel);
+//     in the decode kernel; the column max across lane groups by two
+//     permlane swaps);
 //   * O^T += V^T . P^T: P^T is where the scores left it, V^T comes from
 //     the row-major tile through the transposing LDS read; for bf16, P goes
 //     in as its top 16 bits plus the top 16 bits of the remainder (two
@@ -43,18 +49,15 @@ namespace {
 using namespace mfma;
 
 constexpr int kPWaves = 8;                 // wavefronts per workgroup
-constexpr int kPTile = 32;                 // keys per product tile
-constexpr int kPStage = 64;                // keys staged in LDS per barrier pair
-constexpr int kPRowsW = kPStage / kPWaves; // staged rows each wavefront loads
+constexpr int kPTile = 32;                 // keys per stage (one product tile)
 constexpr int kPD = 128;                   // head dim
-// Padded LDS rows.  K rows (68 dwords) let the 16 lanes of an operand read
-// (rows n = 0..15, 16 bytes each) hit 16 distinct bank groups; V rows (72
-// dwords) let the transposing read's four rows of 8 dwords per 16-lane
-// group fall on disjoint banks.  No single stride does both.
-constexpr int kPRow = kPD * 2 + 16;        // K
-constexpr int kPRowV = kPD * 2 + 32;       // V
+constexpr int kPRowB = kPD * 2;            // bytes of one K or V row
+constexpr int kPHalf = kPTile * kPRowB;    // a stage's K (or V) rows: 8 KB
+constexpr int kPNBuf = 4;                  // stage buffers in the ring
+static_assert(kPNBuf >= 2 && kPNBuf <= 5, "stage ring");
+// V operands read ahead of their product (more spills registers for bf16)
+constexpr int kPVAhead = 1;
 constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
-
 
 struct PrefillArgs {
   void* out;
@@ -70,16 +73,52 @@ struct PrefillArgs {
   float qscale;                            // scale * log2(e)
 };
 
+// Row r of a stage holds its 16-byte chunk c at position c ^ kswz(r) (K) or
+// c ^ vswz(r) (V).  The score product reads 16 rows at one chunk index
+// (lanes n = 0..15): positions c ^ n are all distinct.  The transposing read
+// takes 32 bytes (chunks 2d, 2d + 1) of rows 4q .. 4q+3 per 16 lanes, rows
+// 0..7 per 32: XOR with 2(r & 7) sends the eight rows to eight disjoint
+// 32-byte spans.
+__device__ __forceinline__ uint32_t kswz(uint32_t r) { return r & 15u; }
+__device__ __forceinline__ uint32_t vswz(uint32_t r) { return 2u * (r & 7u); }
+
+// Copy 16 bytes per lane from the buffer resource into LDS: lane l's bytes
+// land at lds + 16 l (lds is wavefront-uniform); an offset past the
+// resource's end writes zeros.
+__device__ __forceinline__ void dma16(rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, static_cast<int>(voff), 0, 0, 0);
+}
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses for the compiler without
+// waiting for the copies still landing in other stage buffers (a memory
+// fence would wait for every outstanding vector-memory operation).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int DT, int BS, int G>
-__global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void prefill_kernel(PrefillArgs a) {
   using T = typename KV<DT>::T;
   constexpr float kNegInf = -INFINITY;
   constexpr int TPW = 16 / G;              // query tokens per wavefront
   constexpr int QT = kPWaves * TPW;        // query tokens per workgroup
   static_assert(BS >= 8 && (BS % 8 == 0), "block size");
 
-  __shared__ __attribute__((aligned(16))) char ks[kPStage * kPRow];
-  __shared__ __attribute__((aligned(16))) char vs[kPStage * kPRowV];
+  // The stage ring: one array per stage, so the compiler can tell a read of
+  // one stage from the copies still landing in the others.  K rows first,
+  // V rows kPHalf bytes on.
+  __shared__ __attribute__((aligned(16))) char sb0[2 * kPHalf];
+  __shared__ __attribute__((aligned(16))) char sb1[2 * kPHalf];
+  __shared__ __attribute__((aligned(16))) char sb2[kPNBuf > 2 ? 2 * kPHalf : 16];
+  __shared__ __attribute__((aligned(16))) char sb3[kPNBuf > 3 ? 2 * kPHalf : 16];
+  __shared__ __attribute__((aligned(16))) char sb4[kPNBuf > 4 ? 2 * kPHalf : 16];
 
   // XCD-aware order.  The hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
@@ -138,6 +177,16 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
       qt[kk] = as_u16x8(col_valid ? v : make_uint4(0, 0, 0, 0));
     }
   }
+  // The scale enters through the exponent's fma, so the running max is
+  // taken over unscaled scores; a negative scale flips the query's signs
+  // (exact) and its magnitude is used, which keeps that max the max of the
+  // scaled scores.
+  const float qs = fabsf(a.qscale);
+  if (a.qscale < 0.f) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qt[kk] = __builtin_bit_cast(u16x8_t, __builtin_bit_cast(u32x4_t, qt[kk]) ^ 0x80008000u);
+  }
 
   float m_run = kNegInf;
   float l_run = 0.f;
@@ -150,171 +199,223 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   const char* kb = static_cast<const char*>(a.key_cache) + static_cast<size_t>(g) * BS * kPD * 2;
   const char* vb = static_cast<const char*>(a.value_cache) + static_cast<size_t>(g) * BS * kPD * 2;
 
-  // Cooperative stage load: wavefront w carries staged rows 8w .. 8w+7 (lane
-  // l: rows 8w + l/16 and 8w + 4 + l/16, 16-byte column l%16).  The eight
-  // rows sit in one block (bs >= 8, stages start at multiples of 64), so one
-  // table entry and one buffer resource per pool serve the wavefront.  The
-  // next stage's loads are issued as soon as the current one is in LDS.
+  // Stage copy: wavefront w carries rows 4w .. 4w+3 of the stage (one 1 KB
+  // run of K and one of V); lane l fills slot l of the run, i.e. row
+  // 4w + l/16 at chunk position l%16, and so reads the row's chunk
+  // (l%16) ^ swz(row).  The four rows sit in one block (bs >= 8, stages start
+  // at multiples of 32), so one table entry and one resource per pool serve
+  // the wavefront.  Rows past kend load zeros without touching memory.
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  constexpr int NJ = kPRowsW / 4;          // 16-lane row groups per wavefront
-  const int lrow = kPRowsW * wv + (lane >> 4);
-  const int lcol = lane & 15;
-  struct Stage {
-    uint4 kr[NJ], vr[NJ];
-  };
-  auto issue = [&](int t0, Stage& st) {
-    const int lb = min(t0 + kPRowsW * wv, max(kend - 1, 0)) / BS;   // wave-uniform
+  const uint32_t lrow = static_cast<uint32_t>(4 * wv + (lane >> 4));
+  const uint32_t lpos = static_cast<uint32_t>(lane & 15);
+  const uint32_t kcol = 16u * (lpos ^ kswz(lrow));
+  const uint32_t vcol = 16u * (lpos ^ vswz(lrow));
+  auto issue = [&](int t0, char* sb) {
+    const int lb = min(t0 + 4 * wv, max(kend - 1, 0)) / BS;   // wave-uniform
+    // a scalar load: a vector load here would make the compiler wait for
+    // every copy in flight before its value could be used
     const int blk = table_entry(trow, lb);
     const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
     const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
     const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
     const rsrc_t kres = make_rsrc(kb + off, bytes);
     const rsrc_t vres = make_rsrc(vb + off, bytes);
+    // row within its block: t0 is a multiple of 32, so for bs <= 32 it is
+    // the stage row mod bs, else the stage's offset plus that row
+    const uint32_t rib = BS > kPTile ? (static_cast<uint32_t>(t0) & (BS - 1)) + lrow : lrow & (BS - 1);
+    const bool in = t0 + static_cast<int>(lrow) < kend;
+    dma16(kres, sb + 1024 * wv, in ? rib * kPRowB + kcol : kOutOfRange);
+    dma16(vres, sb + kPHalf + 1024 * wv, in ? rib * kPRowB + vcol : kOutOfRange);
+  };
+
+  // LDS read offsets of this lane.  Scores: row 16u + n at chunk
+  // (4kk + q4) ^ n.  Transposing read: row vr = 4 q4 + n/4 (and vr + 16),
+  // bytes 32 dt + 8 (n%4) of the row, i.e. chunk 2 dt + (n/2)%2, which sits
+  // at chunk position 2 (dt ^ (vr & 7)) + (n/2)%2.
+  const uint32_t vr = static_cast<uint32_t>(4 * q4 + (n >> 2));
+  const uint32_t vbase = vr * kPRowB + 16u * ((n >> 1) & 1) + 8u * (n & 1);
+  auto v_operand = [&](const char* vs, int dt) {
+    const char* p0 = vs + vbase + 32u * (static_cast<uint32_t>(dt) ^ (vr & 7u));
+    const v4s_t lo = ds_read_tr16(p0);
+    const v4s_t hi = ds_read_tr16(p0 + 16 * kPRowB);
+    return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // scores, softmax and the V product of the stage at t0 held in sb
+  auto compute = [&](int t0, const char* sb) {
+    const char* ks = sb;
+    const char* vs = sb + kPHalf;
+    // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
+    f32x4_t sc[2];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      // row within its block: t0 is a multiple of 64, so for bs <= 64 it is
-      // the lane's staged row mod bs, else the stage's offset plus that row
-      const uint32_t r = static_cast<uint32_t>(lrow + 4 * j);
-      const uint32_t rib = BS > kPStage ? (static_cast<uint32_t>(t0) & (BS - 1)) + r : r & (BS - 1);
-      const uint32_t in = rib * (kPD * 2) + 16u * static_cast<uint32_t>(lcol);
-      const uint32_t voff = t0 + static_cast<int>(r) < kend ? in : kOutOfRange;
-      st.kr[j] = buffer_load16(kres, voff);
-      st.vr[j] = buffer_load16(vres, voff);
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t c = static_cast<uint32_t>(4 * kk + q4) ^ static_cast<uint32_t>(n);
+        const uint4 ka = *reinterpret_cast<const uint4*>(ks + (16 * u + n) * kPRowB + 16 * c);
+        sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
+      }
+    }
+    // the first V operands, read while the softmax runs
+    u16x8_t va[8];
+#pragma unroll
+    for (int dt = 0; dt < kPVAhead; ++dt) va[dt] = v_operand(vs, dt);
+    // Causal mask; rows of blocks outside the pool were loaded as zeros
+    // and count as zero keys and values.  A tile that ends before the
+    // wavefront's first position (all its columns valid) needs no mask.
+    float sv[8];
+    float mt = kNegInf;
+    if (t0 + kPTile - 1 <= wfirst) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[4 * u + i] = sc[u][i];
+          mt = fmaxf(mt, sc[u][i]);
+        }
+    } else {
+      const int lim = col_valid ? pos - t0 : -1;   // rows r <= lim take part
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * u + 4 * q4 + i;
+          const float x = r <= lim ? sc[u][i] : kNegInf;
+          sv[4 * u + i] = x;
+          mt = fmaxf(mt, x);
+        }
+    }
+    // column max over the four lane groups: swap rows of 16 lanes, then
+    // halves of 32
+    {
+      const auto a16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, mt),
+                                                        __builtin_bit_cast(uint32_t, mt), false, false);
+      mt = fmaxf(__builtin_bit_cast(float, a16[0]), __builtin_bit_cast(float, a16[1]));
+      const auto a32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
+                                                        __builtin_bit_cast(uint32_t, mt), false, false);
+      mt = fmaxf(__builtin_bit_cast(float, a32[0]), __builtin_bit_cast(float, a32[1]));
+    }
+    mt *= qs;
+    const bool bump = mt > m_run + kPLazy;
+    const float mn = bump ? mt : m_run;
+    if (__any(bump)) {
+      const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    m_run = mn;
+    // P enters the MFMA in the KV type.  f16 keeps 11 significant bits
+    // and is rounded to nearest.  bf16 keeps 8, so each probability goes
+    // in as two bf16 parts: its top 16 bits (truncation) and the top 16
+    // bits of the exact remainder; both are multiplied in, carrying P to
+    // about 15 bits; the sum adds pv itself (the parts differ from it by
+    // under 2^-14 relative).  Truncation makes each part a bit mask and a
+    // byte permute.
+    // a finite reference: while no key has taken part (mn = -inf) every
+    // score is -inf and exp2(-inf) = 0
+    const float mref = mn == kNegInf ? 0.f : mn;
+    u16x8_t pb, pl;
+    float psum = 0.f;
+    if constexpr (DT == PA_BF16) {
+      uint32_t hb[8], lb[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float pv = fast_exp2(__builtin_fmaf(sv[jj], qs, -mref));
+        const uint32_t b = __builtin_bit_cast(uint32_t, pv);
+        const float hf = __builtin_bit_cast(float, b & 0xffff0000u);
+        hb[jj] = b;
+        lb[jj] = __builtin_bit_cast(uint32_t, pv - hf);   // exact remainder
+        psum += pv;   // the two parts carry pv to within 2^-14 of itself
+      }
+      // upper halves of two words into one: byte selector 0x07060302
+      uint32_t ph[4], pq[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        ph[kq] = __builtin_amdgcn_perm(hb[2 * kq + 1], hb[2 * kq], 0x07060302u);
+        pq[kq] = __builtin_amdgcn_perm(lb[2 * kq + 1], lb[2 * kq], 0x07060302u);
+      }
+      pb = __builtin_bit_cast(u16x8_t, ph);
+      pl = __builtin_bit_cast(u16x8_t, pq);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float pv = fast_exp2(__builtin_fmaf(sv[jj], qs, -mref));
+        const uint16_t hi = to_bits<DT>(pv);
+        pb[jj] = hi;
+        psum += from_bits<DT>(hi);
+      }
+    }
+    l_run += psum;
+
+    // O^T += V^T P^T.  V^T comes from the V rows through the transposing
+    // LDS read (ds_read_b64_tr_b16): within a group of 16 lanes, lane i
+    // receives element i%4 of the 8-byte pieces that lanes 4e + i/4
+    // (e = 0..3) point at.  Lane j of group q4 points at key row
+    // 4*q4 + j/4, dims 16*dt + 4*(j%4), so lane i receives
+    // V[4*q4 + e][16*dt + i]: the A operand's first four entries; the same
+    // read 16 rows down gives the other four.
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt + kPVAhead < 8) va[dt + kPVAhead] = v_operand(vs, dt + kPVAhead);
+      o[dt] = mma<DT>(va[dt], pb, o[dt]);
+      if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va[dt], pl, o[dt]);
     }
   };
 
-  // products of the 32-key tile at t0, staged at LDS row rb
-  auto compute = [&](int t0, int rb) {
-      // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
-      f32x4_t sc[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint4 ka =
-              *reinterpret_cast<const uint4*>(ks + (rb + 16 * u + n) * kPRow + 64 * kk + 16 * q4);
-          sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
-        }
-      }
-      // Causal mask; rows of blocks outside the pool were loaded as zeros
-      // and count as zero keys and values.  A tile that ends before the
-      // wavefront's first position (all its columns valid) needs no mask.
-      float sv[8];
-      float mt = kNegInf;
-      if (t0 + kPTile - 1 <= wfirst) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = sc[u][i] * a.qscale;
-            sv[4 * u + i] = x;
-            mt = fmaxf(mt, x);
-          }
-      } else {
-        const int lim = col_valid ? pos - t0 : -1;   // rows r <= lim take part
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * u + 4 * q4 + i;
-            const float x = r <= lim ? sc[u][i] * a.qscale : kNegInf;
-            sv[4 * u + i] = x;
-            mt = fmaxf(mt, x);
-          }
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const bool bump = mt > m_run + kPLazy;
-      const float mn = bump ? mt : m_run;
-      if (__any(bump)) {
-        const float alpha = bump ? (m_run == kNegInf ? 0.f : fast_exp2(m_run - mn)) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-      }
-      m_run = mn;
-      // P enters the MFMA in the KV type.  f16 keeps 11 significant bits
-      // and is rounded to nearest.  bf16 keeps 8, so each probability goes
-      // in as two bf16 parts: its top 16 bits (truncation) and the top 16
-      // bits of the exact remainder; both are multiplied in, carrying P to
-      // about 15 bits; the sum adds pv itself (the parts differ from it by
-      // under 2^-14 relative).  Truncation makes each part a bit mask and a
-      // byte permute.
-      // a finite reference: while no key has taken part (mn = -inf) every
-      // score is -inf and exp2(-inf - 0) = 0
-      const float mref = mn == kNegInf ? 0.f : mn;
-      u16x8_t pb, pl;
-      float psum = 0.f;
-      if constexpr (DT == PA_BF16) {
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float pv = fast_exp2(sv[jj] - mref);        // exp2(-inf) = 0
-          const uint32_t b = __builtin_bit_cast(uint32_t, pv);
-          const float hf = __builtin_bit_cast(float, b & 0xffff0000u);
-          hb[jj] = b;
-          lb[jj] = __builtin_bit_cast(uint32_t, pv - hf);   // exact remainder
-          psum += pv;   // the two parts carry pv to within 2^-14 of itself
-        }
-        // upper halves of two words into one: byte selector 0x07060302
-        uint32_t ph[4], pq[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ph[k] = __builtin_amdgcn_perm(hb[2 * k + 1], hb[2 * k], 0x07060302u);
-          pq[k] = __builtin_amdgcn_perm(lb[2 * k + 1], lb[2 * k], 0x07060302u);
-        }
-        pb = __builtin_bit_cast(u16x8_t, ph);
-        pl = __builtin_bit_cast(u16x8_t, pq);
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const float pv = fast_exp2(sv[jj] - mref);
-          const uint16_t hi = to_bits<DT>(pv);
-          pb[jj] = hi;
-          psum += from_bits<DT>(hi);
-        }
-      }
-      l_run += psum;
-
-      // O^T += V^T P^T.  V^T comes from the row-major V tile through the
-      // transposing LDS read (ds_read_b64_tr_b16): within a group of 16
-      // lanes, lane i receives element i%4 of the 8-byte chunks that lanes
-      // 4e + i/4 (e = 0..3) point at.  Lane j of group q4 points at key row
-      // 4*q4 + j/4, dims 16*dt + 4*(j%4), so lane i receives
-      // V[4*q4 + e][16*dt + i]: the A operand's first four entries; the same
-      // read 16 rows down gives the other four.
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const u16x8_t va = vt_operand(vs + rb * kPRowV, kPRowV, dt, n, q4);
-        o[dt] = mma<DT>(va, pb, o[dt]);
-        if constexpr (DT == PA_BF16) o[dt] = mma<DT>(va, pl, o[dt]);
-      }
+  // One stage: this wavefront's copies of stage t0 have landed once at most
+  // 2 (kPNBuf - 2) later copies are outstanding; after the barrier every
+  // wavefront's have, and every wavefront is done with stage t0 - 32, whose
+  // buffer takes the copy of stage t0 + 32 (kPNBuf - 1).  Stages past the
+  // wavefront's last position are not computed (their copies still run, to
+  // keep the counts uniform).
+  auto step = [&](int t0, const char* cur, char* refill) {
+    wait_vm<2 * (kPNBuf - 2)>();
+    stage_barrier();
+    issue(t0 + kPTile * (kPNBuf - 1), refill);
+    if (t0 <= wend) compute(t0, cur);
   };
 
-  // one stage: publish the 64 staged keys in LDS, refill the registers with
-  // the next 64 (past kend: zero loads, no traffic), then the two 32-key
-  // product tiles (skipped past the wavefront's last position)
-  Stage st;
-  auto step = [&](int t0) {
-    __syncthreads();                       // every wavefront is done with the last stage
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = lrow + 4 * j;
-      *reinterpret_cast<uint4*>(ks + r * kPRow + 16 * lcol) = st.kr[j];
-      *reinterpret_cast<uint4*>(vs + r * kPRowV + 16 * lcol) = st.vr[j];
+  // The query loads, older than every copy, have returned once the first
+  // stage's copies have.
+  issue(0, sb0);
+  if constexpr (kPNBuf > 2) issue(kPTile, sb1);
+  if constexpr (kPNBuf > 3) issue(2 * kPTile, sb2);
+  if constexpr (kPNBuf > 4) issue(3 * kPTile, sb3);
+  for (int t0 = 0; t0 < kend; t0 += kPNBuf * kPTile) {
+    if constexpr (kPNBuf == 2) {
+      step(t0, sb0, sb1);
+      if (t0 + kPTile >= kend) break;
+      step(t0 + kPTile, sb1, sb0);
+    } else if constexpr (kPNBuf == 3) {
+      step(t0, sb0, sb2);
+      if (t0 + kPTile >= kend) break;
+      step(t0 + kPTile, sb1, sb0);
+      if (t0 + 2 * kPTile >= kend) break;
+      step(t0 + 2 * kPTile, sb2, sb1);
+    } else if constexpr (kPNBuf == 4) {
+      step(t0, sb0, sb3);
+      if (t0 + kPTile >= kend) break;
+      step(t0 + kPTile, sb1, sb0);
+      if (t0 + 2 * kPTile >= kend) break;
+      step(t0 + 2 * kPTile, sb2, sb1);
+      if (t0 + 3 * kPTile >= kend) break;
+      step(t0 + 3 * kPTile, sb3, sb2);
+    } else {
+      step(t0, sb0, sb4);
+      if (t0 + kPTile >= kend) break;
+      step(t0 + kPTile, sb1, sb0);
+      if (t0 + 2 * kPTile >= kend) break;
+      step(t0 + 2 * kPTile, sb2, sb1);
+      if (t0 + 3 * kPTile >= kend) break;
+      step(t0 + 3 * kPTile, sb3, sb2);
+      if (t0 + 4 * kPTile >= kend) break;
+      step(t0 + 4 * kPTile, sb4, sb3);
     }
-    __syncthreads();
-    issue(t0 + kPStage, st);
-    if (t0 <= wend) compute(t0, 0);
-    if (t0 + kPTile <= wend) compute(t0 + kPTile, kPTile);
-  };
-
-  // The query loads (older than the stage's) are waited for before the loop,
-  // where the stage's loads stay in flight.
-  issue(0, st);
-  asm volatile("" ::"v"(qt[0]), "v"(qt[1]), "v"(qt[2]), "v"(qt[3]));
-  for (int t0 = 0; t0 < kend; t0 += kPStage) step(t0);
+  }
+  // No copy may land in LDS after the workgroup has ended.
+  wait_vm<0>();
 
   // column n's sum over the four lane groups, then this lane's four dims of
   // each 16-dim slice
