@@ -13,7 +13,7 @@
 // ordered so each XCD runs whole (s, g) pairs (see the kernel's prologue).  A
 // wavefront owns 16 MFMA columns: 16/G query tokens x the G query heads of
 // KV head g, each column with its own causal limit.  Keys go through LDS in
-// 32-key stages:
+// 64-key stages of two 32-key product tiles:
 //   * a stage's K and V rows are copied from the pool straight into LDS by
 //     the buffer unit (buffer_load_dwordx4 ... lds: each lane's 16 bytes land
 //     at the lane's own slot of a 1 KB run), without passing through
@@ -22,9 +22,10 @@
 //     workgroup barrier.  Rows are stored unpadded with their 16-byte chunks
 //     permuted (XOR of the chunk index with a function of the row), which
 //     keeps both LDS read patterns below free of bank conflicts;
-//   * S^T = K . Q^T (2 x 4 v_mfma_f32_16x16x32): A = K rows from LDS, B = the
-//     wavefront's queries in registers; lane l then holds 8 scores of
-//     column l%16;
+//   * S^T = K . Q^T per tile (2 x 4 v_mfma_f32_16x16x32): A = K rows from
+//     LDS, B = the wavefront's queries in registers; lane l then holds 8
+//     scores of column l%16.  Both tiles' scores are issued first, so the
+//     second tile's products run while the first tile's softmax does;
 //   * causal and validity masks, online softmax per column (lazy rescale as
 //     in the decode kernel; the column max across lane groups by two
 //     permlane swaps);
@@ -49,12 +50,16 @@ namespace {
 using namespace mfma;
 
 constexpr int kPWaves = 8;                 // wavefronts per workgroup
-constexpr int kPTile = 32;                 // keys per stage (one product tile)
+constexpr int kPTile = 32;                 // keys per product tile
+constexpr int kPTPS = 2;                   // product tiles per stage
+constexpr int kPStage = kPTile * kPTPS;    // keys per stage
 constexpr int kPD = 128;                   // head dim
 constexpr int kPRowB = kPD * 2;            // bytes of one K or V row
-constexpr int kPHalf = kPTile * kPRowB;    // a stage's K (or V) rows: 8 KB
-constexpr int kPNBuf = 4;                  // stage buffers in the ring
+constexpr int kPHalf = kPStage * kPRowB;   // a stage's K (or V) rows
+constexpr int kPNBuf = 2;                  // stage buffers in the ring
 static_assert(kPNBuf >= 2 && kPNBuf <= 5, "stage ring");
+constexpr int kPRowsW = kPStage / kPWaves; // stage rows each wavefront copies
+constexpr int kPRuns = kPRowsW / 4;        // 1 KB runs (4 rows) per matrix per wavefront
 // V operands read ahead of their product (more spills registers for bf16)
 constexpr int kPVAhead = 1;
 constexpr float kPLazy = 8.f;              // lazy-rescale threshold (log2 units)
@@ -206,26 +211,32 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
   // at multiples of 32), so one table entry and one resource per pool serve
   // the wavefront.  Rows past kend load zeros without touching memory.
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  const uint32_t lrow = static_cast<uint32_t>(4 * wv + (lane >> 4));
   const uint32_t lpos = static_cast<uint32_t>(lane & 15);
-  const uint32_t kcol = 16u * (lpos ^ kswz(lrow));
-  const uint32_t vcol = 16u * (lpos ^ vswz(lrow));
   auto issue = [&](int t0, char* sb) {
-    const int lb = min(t0 + 4 * wv, max(kend - 1, 0)) / BS;   // wave-uniform
-    // a scalar load: a vector load here would make the compiler wait for
-    // every copy in flight before its value could be used
-    const int blk = table_entry(trow, lb);
-    const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
-    const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
-    const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
-    const rsrc_t kres = make_rsrc(kb + off, bytes);
-    const rsrc_t vres = make_rsrc(vb + off, bytes);
-    // row within its block: t0 is a multiple of 32, so for bs <= 32 it is
-    // the stage row mod bs, else the stage's offset plus that row
-    const uint32_t rib = BS > kPTile ? (static_cast<uint32_t>(t0) & (BS - 1)) + lrow : lrow & (BS - 1);
-    const bool in = t0 + static_cast<int>(lrow) < kend;
-    dma16(kres, sb + 1024 * wv, in ? rib * kPRowB + kcol : kOutOfRange);
-    dma16(vres, sb + kPHalf + 1024 * wv, in ? rib * kPRowB + vcol : kOutOfRange);
+#pragma unroll
+    for (int j = 0; j < kPRuns; ++j) {
+      // rows 4 (kPRuns wv + j) .. +3 of the stage: one block (bs >= 8)
+      const int run = kPRuns * wv + j;
+      const uint32_t lrow = static_cast<uint32_t>(4 * run + (lane >> 4));
+      const int lb = min(t0 + 4 * run, max(kend - 1, 0)) / BS;   // wave-uniform
+      // a scalar load: a vector load here would make the compiler wait for
+      // every copy in flight before its value could be used
+      const int blk = table_entry(trow, lb);
+      const bool bok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.NB);
+      const size_t off = bok ? static_cast<size_t>(blk) * bstride : 0;
+      const uint32_t bytes = bok ? static_cast<uint32_t>(BS * kPD * 2) : 0u;
+      const rsrc_t kres = make_rsrc(kb + off, bytes);
+      const rsrc_t vres = make_rsrc(vb + off, bytes);
+      // row within its block: t0 is a multiple of the stage, so for bs <=
+      // the stage it is the stage row mod bs, else the stage's offset plus
+      // that row
+      const uint32_t rib =
+          BS > kPStage ? (static_cast<uint32_t>(t0) & (BS - 1)) + lrow : lrow & (BS - 1);
+      const bool in = t0 + static_cast<int>(lrow) < kend;
+      dma16(kres, sb + 1024 * run, in ? rib * kPRowB + 16u * (lpos ^ kswz(lrow)) : kOutOfRange);
+      dma16(vres, sb + kPHalf + 1024 * run,
+            in ? rib * kPRowB + 16u * (lpos ^ vswz(lrow)) : kOutOfRange);
+    }
   };
 
   // LDS read offsets of this lane.  Scores: row 16u + n at chunk
@@ -241,12 +252,9 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
     return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // scores, softmax and the V product of the stage at t0 held in sb
-  auto compute = [&](int t0, const char* sb) {
-    const char* ks = sb;
-    const char* vs = sb + kPHalf;
-    // scores: lane (n, q4) gets keys t0 + 16u + 4q4 + i of column n
-    f32x4_t sc[2];
+  // S^T of the 32-key tile whose K rows start at ks: lane (n, q4) gets keys
+  // 16u + 4q4 + i of column n
+  auto scores = [&](const char* ks, f32x4_t (&sc)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       sc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -257,16 +265,15 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
         sc[u] = mma<DT>(as_u16x8(ka), qt[kk], sc[u]);
       }
     }
-    // the first V operands, read while the softmax runs
-    u16x8_t va[8];
-#pragma unroll
-    for (int dt = 0; dt < kPVAhead; ++dt) va[dt] = v_operand(vs, dt);
-    // Causal mask; rows of blocks outside the pool were loaded as zeros
-    // and count as zero keys and values.  A tile that ends before the
-    // wavefront's first position (all its columns valid) needs no mask.
-    float sv[8];
+  };
+
+  // The tile's masked scores (raw) into sv and its column max, scaled.
+  // Causal mask; rows of blocks outside the pool were loaded as zeros and
+  // count as zero keys and values.  A tile that ends before the wavefront's
+  // first position (all its columns valid) needs no mask.
+  auto tile_max = [&](int t0, const f32x4_t (&sc)[2], float (&sv)[8], bool masked) {
     float mt = kNegInf;
-    if (t0 + kPTile - 1 <= wfirst) {
+    if (!masked) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -288,15 +295,20 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
     }
     // column max over the four lane groups: swap rows of 16 lanes, then
     // halves of 32
-    {
-      const auto a16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, mt),
-                                                        __builtin_bit_cast(uint32_t, mt), false, false);
-      mt = fmaxf(__builtin_bit_cast(float, a16[0]), __builtin_bit_cast(float, a16[1]));
-      const auto a32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
-                                                        __builtin_bit_cast(uint32_t, mt), false, false);
-      mt = fmaxf(__builtin_bit_cast(float, a32[0]), __builtin_bit_cast(float, a32[1]));
-    }
-    mt *= qs;
+    const auto a16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, mt),
+                                                      __builtin_bit_cast(uint32_t, mt), false, false);
+    mt = fmaxf(__builtin_bit_cast(float, a16[0]), __builtin_bit_cast(float, a16[1]));
+    const auto a32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
+                                                      __builtin_bit_cast(uint32_t, mt), false, false);
+    mt = fmaxf(__builtin_bit_cast(float, a32[0]), __builtin_bit_cast(float, a32[1]));
+    return mt * qs;
+  };
+
+  // Lazy rescale: the reference max moves only when a tile's max exceeds it
+  // by more than kPLazy (log2 units).  Returns the finite reference the
+  // tile's probabilities are taken against: while no key has taken part
+  // (reference -inf) every score is -inf and exp2(-inf) = 0.
+  auto rescale = [&](float mt) {
     const bool bump = mt > m_run + kPLazy;
     const float mn = bump ? mt : m_run;
     if (__any(bump)) {
@@ -306,17 +318,16 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
       for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
     }
     m_run = mn;
-    // P enters the MFMA in the KV type.  f16 keeps 11 significant bits
-    // and is rounded to nearest.  bf16 keeps 8, so each probability goes
-    // in as two bf16 parts: its top 16 bits (truncation) and the top 16
-    // bits of the exact remainder; both are multiplied in, carrying P to
-    // about 15 bits; the sum adds pv itself (the parts differ from it by
-    // under 2^-14 relative).  Truncation makes each part a bit mask and a
-    // byte permute.
-    // a finite reference: while no key has taken part (mn = -inf) every
-    // score is -inf and exp2(-inf) = 0
-    const float mref = mn == kNegInf ? 0.f : mn;
-    u16x8_t pb, pl;
+    return mn == kNegInf ? 0.f : mn;
+  };
+
+  // P enters the MFMA in the KV type.  f16 keeps 11 significant bits and is
+  // rounded to nearest.  bf16 keeps 8, so each probability goes in as two
+  // bf16 parts: its top 16 bits (truncation) and the top 16 bits of the
+  // exact remainder; both are multiplied in, carrying P to about 15 bits;
+  // the sum adds pv itself (the parts differ from it by under 2^-14
+  // relative).  Truncation makes each part a bit mask and a byte permute.
+  auto probs = [&](const float (&sv)[8], float mref, u16x8_t& pb, u16x8_t& pl) {
     float psum = 0.f;
     if constexpr (DT == PA_BF16) {
       uint32_t hb[8], lb[8];
@@ -346,16 +357,22 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
         pb[jj] = hi;
         psum += from_bits<DT>(hi);
       }
+      pl = pb;
     }
     l_run += psum;
+  };
 
-    // O^T += V^T P^T.  V^T comes from the V rows through the transposing
-    // LDS read (ds_read_b64_tr_b16): within a group of 16 lanes, lane i
-    // receives element i%4 of the 8-byte pieces that lanes 4e + i/4
-    // (e = 0..3) point at.  Lane j of group q4 points at key row
-    // 4*q4 + j/4, dims 16*dt + 4*(j%4), so lane i receives
-    // V[4*q4 + e][16*dt + i]: the A operand's first four entries; the same
-    // read 16 rows down gives the other four.
+  // O^T += V^T P^T.  V^T comes from the V rows through the transposing LDS
+  // read (ds_read_b64_tr_b16): within a group of 16 lanes, lane i receives
+  // element i%4 of the 8-byte pieces that lanes 4e + i/4 (e = 0..3) point
+  // at.  Lane j of group q4 points at key row 4*q4 + j/4, dims
+  // 16*dt + 4*(j%4), so lane i receives V[4*q4 + e][16*dt + i]: the A
+  // operand's first four entries; the same read 16 rows down gives the
+  // other four.
+  auto pv_product = [&](const char* vs, const u16x8_t& pb, const u16x8_t& pl) {
+    u16x8_t va[8];
+#pragma unroll
+    for (int dt = 0; dt < kPVAhead; ++dt) va[dt] = v_operand(vs, dt);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       if (dt + kPVAhead < 8) va[dt + kPVAhead] = v_operand(vs, dt + kPVAhead);
@@ -364,54 +381,76 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
     }
   };
 
+  // one tile: softmax and V product after its scores
+  auto soft_pv = [&](int t0, const f32x4_t (&sc)[2], const char* vs) {
+    float sv[8];
+    const float mref = rescale(tile_max(t0, sc, sv, t0 + kPTile - 1 > wfirst));
+    u16x8_t pb, pl;
+    probs(sv, mref, pb, pl);
+    pv_product(vs, pb, pl);
+  };
+
+  // the stage at t0 held in sb: the scores of all its tiles first, so the
+  // products of one tile overlap the softmax of the one before
+  auto compute = [&](int t0, const char* sb) {
+    f32x4_t sc[kPTPS][2];
+#pragma unroll
+    for (int i = 0; i < kPTPS; ++i)
+      if (i == 0 || t0 + kPTile * i <= wend) scores(sb + kPTile * i * kPRowB, sc[i]);
+#pragma unroll
+    for (int i = 0; i < kPTPS; ++i)
+      if (i == 0 || t0 + kPTile * i <= wend)
+        soft_pv(t0 + kPTile * i, sc[i], sb + kPHalf + kPTile * i * kPRowB);
+  };
+
   // One stage: this wavefront's copies of stage t0 have landed once at most
-  // 2 (kPNBuf - 2) later copies are outstanding; after the barrier every
-  // wavefront's have, and every wavefront is done with stage t0 - 32, whose
-  // buffer takes the copy of stage t0 + 32 (kPNBuf - 1).  Stages past the
-  // wavefront's last position are not computed (their copies still run, to
-  // keep the counts uniform).
+  // 2 kPRuns (kPNBuf - 2) later copies are outstanding; after the barrier
+  // every wavefront's have, and every wavefront is done with the previous
+  // stage, whose buffer takes the copy of the stage kPNBuf - 1 ahead.
+  // Stages past the wavefront's last position are not computed (their
+  // copies still run, to keep the counts uniform).
   auto step = [&](int t0, const char* cur, char* refill) {
-    wait_vm<2 * (kPNBuf - 2)>();
+    wait_vm<2 * kPRuns * (kPNBuf - 2)>();
     stage_barrier();
-    issue(t0 + kPTile * (kPNBuf - 1), refill);
+    issue(t0 + kPStage * (kPNBuf - 1), refill);
     if (t0 <= wend) compute(t0, cur);
   };
 
   // The query loads, older than every copy, have returned once the first
   // stage's copies have.
   issue(0, sb0);
-  if constexpr (kPNBuf > 2) issue(kPTile, sb1);
-  if constexpr (kPNBuf > 3) issue(2 * kPTile, sb2);
-  if constexpr (kPNBuf > 4) issue(3 * kPTile, sb3);
-  for (int t0 = 0; t0 < kend; t0 += kPNBuf * kPTile) {
+  if constexpr (kPNBuf > 2) issue(kPStage, sb1);
+  if constexpr (kPNBuf > 3) issue(2 * kPStage, sb2);
+  if constexpr (kPNBuf > 4) issue(3 * kPStage, sb3);
+  for (int t0 = 0; t0 < kend; t0 += kPNBuf * kPStage) {
     if constexpr (kPNBuf == 2) {
       step(t0, sb0, sb1);
-      if (t0 + kPTile >= kend) break;
-      step(t0 + kPTile, sb1, sb0);
+      if (t0 + kPStage >= kend) break;
+      step(t0 + kPStage, sb1, sb0);
     } else if constexpr (kPNBuf == 3) {
       step(t0, sb0, sb2);
-      if (t0 + kPTile >= kend) break;
-      step(t0 + kPTile, sb1, sb0);
-      if (t0 + 2 * kPTile >= kend) break;
-      step(t0 + 2 * kPTile, sb2, sb1);
+      if (t0 + kPStage >= kend) break;
+      step(t0 + kPStage, sb1, sb0);
+      if (t0 + 2 * kPStage >= kend) break;
+      step(t0 + 2 * kPStage, sb2, sb1);
     } else if constexpr (kPNBuf == 4) {
       step(t0, sb0, sb3);
-      if (t0 + kPTile >= kend) break;
-      step(t0 + kPTile, sb1, sb0);
-      if (t0 + 2 * kPTile >= kend) break;
-      step(t0 + 2 * kPTile, sb2, sb1);
-      if (t0 + 3 * kPTile >= kend) break;
-      step(t0 + 3 * kPTile, sb3, sb2);
+      if (t0 + kPStage >= kend) break;
+      step(t0 + kPStage, sb1, sb0);
+      if (t0 + 2 * kPStage >= kend) break;
+      step(t0 + 2 * kPStage, sb2, sb1);
+      if (t0 + 3 * kPStage >= kend) break;
+      step(t0 + 3 * kPStage, sb3, sb2);
     } else {
       step(t0, sb0, sb4);
-      if (t0 + kPTile >= kend) break;
-      step(t0 + kPTile, sb1, sb0);
-      if (t0 + 2 * kPTile >= kend) break;
-      step(t0 + 2 * kPTile, sb2, sb1);
-      if (t0 + 3 * kPTile >= kend) break;
-      step(t0 + 3 * kPTile, sb3, sb2);
-      if (t0 + 4 * kPTile >= kend) break;
-      step(t0 + 4 * kPTile, sb4, sb3);
+      if (t0 + kPStage >= kend) break;
+      step(t0 + kPStage, sb1, sb0);
+      if (t0 + 2 * kPStage >= kend) break;
+      step(t0 + 2 * kPStage, sb2, sb1);
+      if (t0 + 3 * kPStage >= kend) break;
+      step(t0 + 3 * kPStage, sb3, sb2);
+      if (t0 + 4 * kPStage >= kend) break;
+      step(t0 + 4 * kPStage, sb4, sb3);
     }
   }
   // No copy may land in LDS after the workgroup has ended.
