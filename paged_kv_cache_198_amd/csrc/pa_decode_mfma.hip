@@ -29,7 +29,7 @@
 //     in registers (lane l: head l%16, zero for the padding heads).  Lane l
 //     then holds the scores of tokens 4(l/16) + i (i = 0..3) for head l%16.
 //   * online softmax per head (max across the 4 lane groups of a head with
-//     two shuffles; the running sum stays per lane and is added up at the
+//     two permlane swaps; the running sum stays per lane and is added up at the
 //     end); the reference max moves only when it grows by more than 2^8, so
 //     the accumulators are rarely rescaled.
 //   * O^T += V^T . P^T on v_mfma_f32_16x16x16 (K = the tile's 16 tokens):
@@ -296,8 +296,7 @@ void decode_gqa_mfma_kernel(DecodeArgs a) {
         sv[4 * u + i] = x;
         mt = fmaxf(mt, x);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_lane_groups(mt);
     // Lazy rescale: the reference max moves only when the tile's max exceeds
     // it by more than kLazy (log2 units), so weights stay <= 2^kLazy and the
     // accumulators are rarely touched.

@@ -76,6 +76,20 @@ __device__ __forceinline__ void lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Max of x over lanes l, l^16, l^32 and l^48 (the four lane groups that hold
+// one MFMA column), on the VALU: v_permlane16_swap exchanges rows 1 and 3
+// of one copy with rows 0 and 2 of the other (a row is 16 lanes), so the
+// max of the two copies is the max over lanes l and l^16; the 32-lane
+// halves the same way.  Needs every lane active.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  const auto a16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, a16[0]), __builtin_bit_cast(float, a16[1]));
+  const auto a32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, a32[0]), __builtin_bit_cast(float, a32[1]));
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x7ffffff0u;   // past every resource's end
 

@@ -293,15 +293,8 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
           mt = fmaxf(mt, x);
         }
     }
-    // column max over the four lane groups: swap rows of 16 lanes, then
-    // halves of 32
-    const auto a16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, mt),
-                                                      __builtin_bit_cast(uint32_t, mt), false, false);
-    mt = fmaxf(__builtin_bit_cast(float, a16[0]), __builtin_bit_cast(float, a16[1]));
-    const auto a32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt),
-                                                      __builtin_bit_cast(uint32_t, mt), false, false);
-    mt = fmaxf(__builtin_bit_cast(float, a32[0]), __builtin_bit_cast(float, a32[1]));
-    return mt * qs;
+    // column max over the four lane groups
+    return max_lane_groups(mt) * qs;
   };
 
   // Lazy rescale: the reference max moves only when a tile's max exceeds it
