@@ -20,9 +20,11 @@ runs every measurement in a child process of its own, one after another:
   * the block-size sweep of that batch (8, 32, 64, 128), one process each;
   * every other workload (tiny, LLaMA-7B-shaped, shared-prefix parallel
     sampling at 504- and 512-token prompts, long-context grouped-query), each
-    with its own oracle baseline.
+    with its own oracle baseline;
+  * paged prefill of 16 LLaMA-13B-shaped prompts, with its oracle baseline.
 One JSON line merges them: the headline's fields at the top level, the sweep
-under ``sweep``, the others under ``configs``.  ``value`` is algorithmic KV
+under ``sweep``, the others under ``configs``, the prefill under
+``prefill``.  ``value`` is algorithmic KV
 bytes (every attended token's K and V row once per head) per second of whole
 step; ``roofline`` prices the attention launch alone (its average duration
 from HIP events around it) against the 8 TB/s HBM peak;
@@ -599,6 +601,11 @@ def run_prefill(args, pa, synth, torch):
     out = torch.empty_like(w.q)
     mq = int(w.chunk_lens.max())
     stream = torch.cuda.current_stream()
+    # the oracle's host inputs, copied before any GPU step writes the pools
+    oracle_in = None if args.no_cpu_baseline else {
+        "q": synth.to_numpy_storage(w.q), "nk": synth.to_numpy_storage(w.new_key),
+        "nv": synth.to_numpy_storage(w.new_value), "kc": synth.to_numpy_storage(kc).copy(),
+        "vc": synth.to_numpy_storage(vc).copy()}
 
     def step():
         pa.pa_reshape_and_cache(w.new_key, w.new_value, kc, vc, slots)
@@ -660,8 +667,57 @@ def run_prefill(args, pa, synth, torch):
                              "cache write; back_to_back_us: repeated launches with K/V "
                              "still cached"},
         "back_to_back_us": warm_ms * 1e3,
-        "cpu_baseline": None,
+        "cpu_baseline": None if oracle_in is None else cpu_baseline_prefill(
+            w, oracle_in, out, args.cpu_budget),
     }
+
+
+def cpu_baseline_prefill(w, h, gpu_out, budget_s=8.0):
+    """The float64 oracle on the host over the same prefill step: the cache
+    write of every prompt token (slots from the oracle's own walk of the
+    block tables) and causal attention, on the inputs copied before the
+    first GPU step.  All prompts when a step fits about ``budget_s``
+    seconds, else the first ones (value scaled by their tokens).  Also the
+    largest difference from the GPU's output on those prompts."""
+    import oracle.decode as od
+    from paged_kv_cache_198_amd import synth
+    S = w.S
+    n = w.chunk_lens.astype(np.int64)
+    ctx = w.context_lens.astype(np.int64)
+    slots = [od.slot_of(w.block_tables[s], int(p), w.bs)
+             for s in range(S) for p in range(int(ctx[s] - n[s]), int(ctx[s]))]
+    od.reshape_and_cache(h["nk"], h["nv"], h["kc"], h["vc"], slots, inplace=True)
+
+    def run(seqs):
+        t0 = time.perf_counter()
+        o = od.paged_prefill(h["q"], h["kc"], h["vc"], w.block_tables, w.context_lens,
+                             w.query_start, w.scale, w.dtype, seqs=seqs)
+        return time.perf_counter() - t0, o
+
+    # the cost of the first prompt sets the sample
+    t_first, _ = run([0])
+    per_tok = t_first / max(int(n[0]) ** 2, 1)           # causal work grows as n^2
+    seqs, total = [], 0.0
+    for s in range(S):
+        est = per_tok * float(n[s]) ** 2
+        if seqs and total + est > budget_s:
+            break
+        seqs.append(s)
+        total += est
+    secs, ref = run(seqs)
+    toks = int(n[seqs].sum())
+    rows = np.concatenate([np.arange(w.query_start[s], w.query_start[s + 1]) for s in seqs])
+    got = od.widen(synth.to_numpy_storage(gpu_out)[rows], w.dtype)
+    cores, blas = host_threads()
+    sf = sum(4 * w.D * w.Hq * int((ctx[s] - n[s] + 1 + ctx[s]) * n[s] // 2) for s in seqs)
+    what = (f"the whole prefill step ({S} prompts)" if len(seqs) == S else
+            f"the first {len(seqs)} of {S} prompts ({toks} of {w.T} tokens); value scaled by "
+            "their tokens")
+    return {"value": toks / secs, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "s_for_sample": secs, "tflops": sf / secs / 1e12, "host_cores": cores,
+            "blas_threads": blas,
+            "sample": what + "; float64 numpy, cache write untimed (done once before)",
+            "max_abs_err_vs_gpu": float(np.max(np.abs(got - ref[rows])))}
 
 
 BEAM_BENCH = dict(requests=16, width=4, layers=40, Hq=40, Hkv=40, D=128, dtype="bf16", bs=16,
@@ -978,6 +1034,16 @@ def shared_summary(r):
             "cpu_baseline": r["cpu_baseline"]}
 
 
+def prefill_summary(r):
+    """The prefill record kept in the default line."""
+    return {"workload": r["config"]["workload"], "dtype": r["dtype"],
+            "us_per_step": r["us_per_step"], "prompt_tokens_per_s": r["value"],
+            "kernel": r["roofline"]["kernel"], "kernel_us": r["roofline"]["kernel_us"],
+            "TFLOPs": r["roofline"]["achieved"], "frac_bf16_mfma_peak": r["roofline"]["frac"],
+            "back_to_back_us": r["back_to_back_us"], "flops_per_step": r["config"]["flops_per_step"],
+            "cpu_baseline": r["cpu_baseline"]}
+
+
 def launcher(args):
     """The default run.  This process never touches the GPU: every
     measurement runs in a child process, one after another.  A child that
@@ -1030,6 +1096,14 @@ def launcher(args):
                 line["configs"][key] = decode_summary(r)
         line["sweep"]["note"] = ("each block size in a process of its own, after the "
                                  f"headline (bs {args.bs})")
+        # paged prefill of a 13B-shaped prompt batch (causal attention over
+        # the blocks the prompts were written to)
+        r, err = child(["--workload", "prefill"])
+        if err:
+            line["error"] = err
+            print(json.dumps(line), flush=True)
+            sys.exit(1)
+        line["prefill"] = prefill_summary(r)
     print(json.dumps(line), flush=True)
 
 

@@ -71,3 +71,33 @@ def test_oracle_step_baseline_on_host_tensors():
     assert np.isfinite(rec["max_abs_err_vs_gpu"]) and rec["max_abs_err_vs_gpu"] < 2e-2
     out[1, 0, 0] += 1.0
     assert bench.OracleStep(step, budget_s=0.2).time(gpu_out=out)["max_abs_err_vs_gpu"] > 0.5
+
+
+def test_prefill_baseline_on_host_tensors():
+    # the prefill baseline on a small prompt batch: it writes the prompt rows
+    # itself (the pools hold NaN at those slots), runs the oracle and reports
+    # the largest difference from the output it is handed
+    import numpy as np
+    import torch
+    import oracle.decode as od
+    from paged_kv_cache_198_amd import synth
+    bench = _bench_module()
+    w = synth.make_prefill(2, device="cpu", S=3, Hq=4, Hkv=2, bs=16, pool_tokens=2048,
+                           prefix=("fixed", [0, 5, 17]), chunk=("fixed", [20, 33, 9]))
+    h = {"q": synth.to_numpy_storage(w.q), "nk": synth.to_numpy_storage(w.new_key),
+         "nv": synth.to_numpy_storage(w.new_value),
+         "kc": synth.to_numpy_storage(w.key_cache).copy(),
+         "vc": synth.to_numpy_storage(w.value_cache).copy()}
+    slots = [od.slot_of(w.block_tables[s], p, w.bs) for s in range(w.S)
+             for p in range(int(w.context_lens[s] - w.chunk_lens[s]), int(w.context_lens[s]))]
+    kc, vc = od.reshape_and_cache(h["nk"], h["nv"], h["kc"], h["vc"], slots)
+    want = od.paged_prefill(h["q"], kc, vc, w.block_tables, w.context_lens, w.query_start,
+                            w.scale, w.dtype)
+    out = torch.from_numpy(want).to(w.q.dtype)
+    h2 = {k: v.copy() for k, v in h.items()}
+    rec = bench.cpu_baseline_prefill(w, h, out, budget_s=5.0)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["value"] > 0
+    assert "whole prefill step (3 prompts)" in rec["sample"]
+    assert rec["max_abs_err_vs_gpu"] < 2e-2
+    out[int(w.query_start[1]), 0, 0] += 1.0
+    assert bench.cpu_baseline_prefill(w, h2, out, budget_s=5.0)["max_abs_err_vs_gpu"] > 0.5
