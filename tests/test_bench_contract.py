@@ -101,3 +101,22 @@ def test_prefill_baseline_on_host_tensors():
     assert rec["max_abs_err_vs_gpu"] < 2e-2
     out[int(w.query_start[1]), 0, 0] += 1.0
     assert bench.cpu_baseline_prefill(w, h2, out, budget_s=5.0)["max_abs_err_vs_gpu"] > 0.5
+
+
+def test_beam_baseline_on_host_arrays():
+    # the beam baseline on a small stack: its own allocator drive from the
+    # starting state, one step, a positive rate and a per-layer estimate
+    import numpy as np
+    bench = _bench_module()
+    c = dict(requests=3, width=3, layers=5, Hq=4, Hkv=2, D=16, dtype="f16", bs=8, NB=256)
+    rng = np.random.default_rng(0)
+    plens = np.array([13, 8, 21])
+    S = c["requests"] * c["width"]
+    h = {"pk": rng.standard_normal((21, 2, 16)).astype(np.float16),
+         "nk": rng.standard_normal((S, 2, 16)).astype(np.float16),
+         "q": rng.standard_normal((S, 4, 16)).astype(np.float16)}
+    pick0 = [[0, 0, 1], [2, 2, 2], [0, 1, 2]]
+    rec = bench.cpu_baseline_beam(c, plens, h, pick0, 0.25, 0)
+    assert rec["kind"] == "oracle" and rec["value"] > 0
+    assert np.isclose(rec["s_per_step_estimate"], rec["host_s"] + 5 * rec["layer_s"])
+    assert "layer 0 of 5" in rec["sample"] and "9 beams" in rec["sample"]
