@@ -17,11 +17,11 @@
 //   * a stage's K and V rows are copied from the pool straight into LDS by
 //     the buffer unit (buffer_load_dwordx4 ... lds: each lane's 16 bytes land
 //     at the lane's own slot of a 1 KB run), without passing through
-//     registers.  kPNBuf stage buffers form a ring, so the loads of the next
-//     kPNBuf - 1 stages are in flight while one is used; each stage costs one
-//     workgroup barrier.  Rows are stored unpadded with their 16-byte chunks
-//     permuted (XOR of the chunk index with a function of the row), which
-//     keeps both LDS read patterns below free of bank conflicts;
+//     registers.  Two stage buffers alternate, so the next stage's copies
+//     are in flight while one is used; each stage costs one workgroup
+//     barrier.  Rows are stored unpadded with their 16-byte chunks permuted
+//     (XOR of the chunk index with a function of the row), which keeps both
+//     LDS read patterns below free of bank conflicts;
 //   * S^T = K . Q^T per tile (2 x 4 v_mfma_f32_16x16x32): A = K rows from
 //     LDS, B = the wavefront's queries in registers; lane l then holds 8
 //     scores of column l%16.  Both tiles' scores are issued first, so the
@@ -56,8 +56,6 @@ constexpr int kPStage = kPTile * kPTPS;    // keys per stage
 constexpr int kPD = 128;                   // head dim
 constexpr int kPRowB = kPD * 2;            // bytes of one K or V row
 constexpr int kPHalf = kPStage * kPRowB;   // a stage's K (or V) rows
-constexpr int kPNBuf = 2;                  // stage buffers in the ring
-static_assert(kPNBuf >= 2 && kPNBuf <= 5, "stage ring");
 constexpr int kPRowsW = kPStage / kPWaves; // stage rows each wavefront copies
 constexpr int kPRuns = kPRowsW / 4;        // 1 KB runs (4 rows) per matrix per wavefront
 // V operands read ahead of their product (more spills registers for bf16)
@@ -116,14 +114,11 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
   constexpr int QT = kPWaves * TPW;        // query tokens per workgroup
   static_assert(BS >= 8 && (BS % 8 == 0), "block size");
 
-  // The stage ring: one array per stage, so the compiler can tell a read of
-  // one stage from the copies still landing in the others.  K rows first,
+  // The two stage buffers: one array each, so the compiler can tell a read
+  // of one stage from the copies still landing in the other.  K rows first,
   // V rows kPHalf bytes on.
   __shared__ __attribute__((aligned(16))) char sb0[2 * kPHalf];
   __shared__ __attribute__((aligned(16))) char sb1[2 * kPHalf];
-  __shared__ __attribute__((aligned(16))) char sb2[kPNBuf > 2 ? 2 * kPHalf : 16];
-  __shared__ __attribute__((aligned(16))) char sb3[kPNBuf > 3 ? 2 * kPHalf : 16];
-  __shared__ __attribute__((aligned(16))) char sb4[kPNBuf > 4 ? 2 * kPHalf : 16];
 
   // XCD-aware order.  The hardware hands consecutive workgroups to the 8
   // XCDs in turn, each with its own L2.  Pair p = (sequence, KV head) goes to
@@ -396,55 +391,25 @@ __global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(4)
         soft_pv(t0 + kPTile * i, sc[i], sb + kPHalf + kPTile * i * kPRowB);
   };
 
-  // One stage: this wavefront's copies of stage t0 have landed once at most
-  // 2 kPRuns (kPNBuf - 2) later copies are outstanding; after the barrier
-  // every wavefront's have, and every wavefront is done with the previous
-  // stage, whose buffer takes the copy of the stage kPNBuf - 1 ahead.
-  // Stages past the wavefront's last position are not computed (their
-  // copies still run, to keep the counts uniform).
+  // One stage: this wavefront's copies of stage t0 have landed (nothing
+  // else is outstanding); after the barrier every wavefront's have, and
+  // every wavefront is done with the previous stage, whose buffer takes the
+  // copy of the next one.  Stages past the wavefront's last position are
+  // not computed (their copies still run, to keep the counts uniform).
   auto step = [&](int t0, const char* cur, char* refill) {
-    wait_vm<2 * kPRuns * (kPNBuf - 2)>();
+    wait_vm<0>();
     stage_barrier();
-    issue(t0 + kPStage * (kPNBuf - 1), refill);
+    issue(t0 + kPStage, refill);
     if (t0 <= wend) compute(t0, cur);
   };
 
   // The query loads, older than every copy, have returned once the first
   // stage's copies have.
   issue(0, sb0);
-  if constexpr (kPNBuf > 2) issue(kPStage, sb1);
-  if constexpr (kPNBuf > 3) issue(2 * kPStage, sb2);
-  if constexpr (kPNBuf > 4) issue(3 * kPStage, sb3);
-  for (int t0 = 0; t0 < kend; t0 += kPNBuf * kPStage) {
-    if constexpr (kPNBuf == 2) {
-      step(t0, sb0, sb1);
-      if (t0 + kPStage >= kend) break;
-      step(t0 + kPStage, sb1, sb0);
-    } else if constexpr (kPNBuf == 3) {
-      step(t0, sb0, sb2);
-      if (t0 + kPStage >= kend) break;
-      step(t0 + kPStage, sb1, sb0);
-      if (t0 + 2 * kPStage >= kend) break;
-      step(t0 + 2 * kPStage, sb2, sb1);
-    } else if constexpr (kPNBuf == 4) {
-      step(t0, sb0, sb3);
-      if (t0 + kPStage >= kend) break;
-      step(t0 + kPStage, sb1, sb0);
-      if (t0 + 2 * kPStage >= kend) break;
-      step(t0 + 2 * kPStage, sb2, sb1);
-      if (t0 + 3 * kPStage >= kend) break;
-      step(t0 + 3 * kPStage, sb3, sb2);
-    } else {
-      step(t0, sb0, sb4);
-      if (t0 + kPStage >= kend) break;
-      step(t0 + kPStage, sb1, sb0);
-      if (t0 + 2 * kPStage >= kend) break;
-      step(t0 + 2 * kPStage, sb2, sb1);
-      if (t0 + 3 * kPStage >= kend) break;
-      step(t0 + 3 * kPStage, sb3, sb2);
-      if (t0 + 4 * kPStage >= kend) break;
-      step(t0 + 4 * kPStage, sb4, sb3);
-    }
+  for (int t0 = 0; t0 < kend; t0 += 2 * kPStage) {
+    step(t0, sb0, sb1);
+    if (t0 + kPStage >= kend) break;
+    step(t0 + kPStage, sb1, sb0);
   }
   // No copy may land in LDS after the workgroup has ended.
   wait_vm<0>();
