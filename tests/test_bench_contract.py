@@ -120,3 +120,15 @@ def test_beam_baseline_on_host_arrays():
     assert rec["kind"] == "oracle" and rec["value"] > 0
     assert np.isclose(rec["s_per_step_estimate"], rec["host_s"] + 5 * rec["layer_s"])
     assert "layer 0 of 5" in rec["sample"] and "9 beams" in rec["sample"]
+
+
+def test_system_prompt_baseline_on_host_tensors():
+    # the system-prompt baseline on a small script: its own allocator and
+    # registry drive, then one timed decode step with a positive rate
+    bench = _bench_module()
+    from paged_kv_cache_198_amd import synth
+    sc = synth.make_system_prompt(seed=1, device="cpu", requests=3, Hq=4, Hkv=2, D=32, NB=256,
+                                  system_len=40, own=(0, 20))
+    rec = bench.cpu_baseline_system_prompt(sc)
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["reps"] == 1
+    assert "registry" in rec["sample"]
