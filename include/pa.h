@@ -3,13 +3,15 @@
  * (gfx950).
  *
  * What is computed.  "PagedAttention: the KV cache was the bottleneck all
- * along", section "Virtual memory for attention": the KV cache is cut into
- * fixed-size blocks holding the keys and values of a fixed number of tokens;
- * a per-sequence block table maps logical blocks to physical blocks that need
- * not be adjacent, as a page table maps virtual to physical pages; a sequence
- * acquires blocks as it grows; the attention kernel gathers keys and values
- * from the scattered blocks; completions of one prompt share its blocks and
- * copy one only when they diverge (copy-on-write).  The abstract of
+ * along", section "Virtual memory for attention": the KV cache is split into
+ * equal-sized blocks, each storing keys and values for the same number of
+ * tokens; each sequence has a block table from its logical block indices to
+ * physical blocks that may sit anywhere in the pool (the paging analogy of an
+ * operating system); a block is added to a sequence only when its length
+ * reaches into it; attention reads keys and values through the table from
+ * wherever the blocks sit; completions of one prompt point at the prompt's
+ * blocks and get a private copy of a block only when they write different
+ * tokens into it (copy-on-write).  The abstract of
  * "Efficient Memory Management for Large Language Model Serving with
  * PagedAttention" names the same two properties (near-zero KV waste,
  * sharing within and across requests).
@@ -391,8 +393,9 @@ int pa_build_batch(const pa_allocator* a, const int64_t* seq_ids, int32_t S, int
                    int32_t* block_tables, int32_t* context_lens);
 
 /* Prefix registry: sharing across requests ("From the abstract": the cache
- * is shared within and across requests; "What is left": shared blocks for
- * common system prompts across users).  The registry maps 64-bit keys to
+ * is shared within and across requests; "What is left": the pages ask for the
+ * prompt side to reuse blocks as well, e.g. one system prompt held once for
+ * many users).  The registry maps 64-bit keys to
  * full blocks and holds one reference to each, so a registered block
  * outlives the sequence that filled it.  Keys come from the caller, one per
  * block, and must name the whole prefix up to and including that block

@@ -8,8 +8,8 @@ What the pages fix ("PagedAttention: the KV cache was the bottleneck all
 along", section "Virtual memory for attention"):
   * the cache is cut into fixed-size blocks of ``bs`` tokens; a per-sequence
     block table maps logical blocks to physical ones;
-  * a sequence acquires blocks as it grows (memory is allocated on demand),
-    so only its last block can be partly empty;
+  * a block is taken from the pool only when a sequence's length reaches
+    into it, so only its last block can be partly empty;
   * completions of one prompt share the prompt's blocks and copy a block only
     when they diverge (copy-on-write); beams are forked and discarded.
 
@@ -27,8 +27,8 @@ Readings where the pages are silent:
 Sharing across requests (page "Efficient Memory Management for Large
 Language Model Serving with PagedAttention", from the abstract: sharing
 within and across requests; "PagedAttention: the KV cache was the
-bottleneck all along", section "What is left": shared blocks for common
-system prompts across users).  Readings:
+bottleneck all along", section "What is left": prompt-side reuse of blocks,
+e.g. one system prompt held once for many users).  Readings:
   * a registry maps caller keys (one per block, naming the whole prefix up
     to that block) to full blocks and holds one reference to each;
   * ``publish`` enters a sequence's first n full blocks; a key already
