@@ -646,6 +646,59 @@ def test_fused_step_clamped_lengths(name, over, part):
     assert err <= TOL[w.dtype]
 
 
+ZERO_CASES = [  # vector-ALU (MHA and grouped) and matrix-core kernels, one pass and split
+    ("llama7b", dict(S=6, NB=512, Hq=4, Hkv=4, lengths=("fixed", [0, 17, 0, 300, 1, 0])), 0),
+    ("llama7b", dict(S=6, NB=512, Hq=8, Hkv=2, D=64, dtype="bf16",
+                     lengths=("fixed", [0, 700, 0, 33, 1, 0])), 64),
+    ("long_gqa", dict(S=5, NB=512, lengths=("fixed", [0, 700, 0, 1, 2500])), 0),
+    ("long_gqa", dict(S=5, NB=512, lengths=("fixed", [0, 700, 0, 1, 2500])), 512),
+    ("long_gqa", dict(S=4, NB=64, bs=8, dtype="f16", lengths=("fixed", [0, 0, 0, 0])), 64),
+]
+
+
+@pytest.mark.parametrize("name,over,part", ZERO_CASES)
+def test_zero_length_contexts(name, over, part):
+    """Sequences with no tokens get an all-zero output and no stored row;
+    the others match the oracle; the fused step equals the two calls bit for
+    bit, pools included (an all-empty batch too)."""
+    w = synth.make_decode(name, device=DEV, **over)
+    alloc = pa.Allocator(w.NB, w.bs, init_order=w.block_order)
+    step = np.full(w.S, -1, dtype=np.int64)
+    for s in range(w.S):
+        alloc.create(s)
+        n = int(w.context_lens[s])
+        if n:
+            slots, _, _ = alloc.append_n(s, n)
+            step[s] = slots[-1]
+    tables, lens = alloc.build_batch(list(range(w.S)), w.MB)
+    assert np.array_equal(tables, w.block_tables) and np.array_equal(lens, w.context_lens)
+    mx = max(1, int(lens.max()))
+    note(f"case zero-length {name} {over} part={part} lens={lens.tolist()}")
+    t_d, l_d = torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV)
+    ws = pa.make_workspace(w.S, w.Hq, w.D, mx, part)
+    kc1, vc1 = w.key_cache.clone(), w.value_cache.clone()
+    out1 = torch.full((w.S, w.Hq, w.D), float("nan"), dtype=w.q.dtype, device=DEV)
+    pa.pa_reshape_and_cache(w.new_key, w.new_value, kc1, vc1, torch.from_numpy(step).to(DEV))
+    pa.pa_decode_attention(out1, w.q, kc1, vc1, t_d, l_d, mx, w.scale, part, ws)
+    kc2, vc2 = w.key_cache.clone(), w.value_cache.clone()
+    out2 = torch.full_like(out1, float("nan"))
+    pa.pa_decode_step(out2, w.q, w.new_key, w.new_value, kc2, vc2, t_d, l_d, mx, w.scale, part,
+                      ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out1), bits(out2))
+    assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+    got = widened(out2, w.dtype)
+    empty = [s for s in range(w.S) if lens[s] == 0]
+    full = [s for s in range(w.S) if lens[s] > 0]
+    assert np.array_equal(got[empty], np.zeros_like(got[empty]))      # exact zeros
+    if full:
+        ref, oslots = oracle_step(w, full)
+        assert np.array_equal(step[full], oslots)
+        err = float(np.max(np.abs(got[full] - ref)))
+        note(f"  max abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+
+
 # ---------------------------------------------------------------------------
 # the engine (allocator + kernels sequenced in Python) against the oracle's own
 # drive of the same shared-prefix script
