@@ -13,10 +13,22 @@
 
 namespace pa {
 
+// Bytes of K and V rows up to which the cache write streams its stores out
+// with the non-temporal hint: the 8 XCDs' L2s hold 32 MiB.  A decode step's
+// rows (a few MB scattered over the pool) stored the default way stay dirty
+// in the L2s and are written back when the launch ends; streamed, the
+// two-call decode step measured about 1% faster.  A prompt fill (hundreds of
+// MB) keeps the default policy, under which the prefill step that follows
+// measured faster.
+constexpr int64_t kStreamWriteMax = int64_t(32) << 20;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 // "Virtual memory for attention": a new token's key and value rows go to the
 // slot its sequence's block table gives it.  One thread per 16-byte chunk of
 // the [T][Hkv][D] inputs; chunk c of (t, h) lands at
 // ((slot/bs * Hkv + h) * bs + slot%bs) * cpr + c in the [NB][Hkv][bs][D] pool.
+template <bool NT>
 __global__ __launch_bounds__(256) void cache_write_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value,
     uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
@@ -33,8 +45,16 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
   const int64_t blk = slot / bs;
   const int64_t off = slot - blk * bs;
   const int64_t dst = ((blk * Hkv + h) * bs + off) * cpr + c;
-  key_cache[dst] = key[i];
-  value_cache[dst] = value[i];
+  if constexpr (NT) {
+    const uint4 k = key[i], v = value[i];
+    __builtin_nontemporal_store(u32x4_t{k.x, k.y, k.z, k.w},
+                                reinterpret_cast<u32x4_t*>(key_cache + dst));
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                reinterpret_cast<u32x4_t*>(value_cache + dst));
+  } else {
+    key_cache[dst] = key[i];
+    value_cache[dst] = value[i];
+  }
 }
 
 // Copy-on-write: pairs and per-layer pool pointers travel in the kernel
@@ -78,7 +98,9 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* ke
   const int64_t total = static_cast<int64_t>(T) * Hkv * cpr;
   const int64_t blocks = (total + 255) / 256;
   if (blocks > 0x7fffffff) return PA_ERR_INVALID;
-  hipLaunchKernelGGL(pa::cache_write_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+  const bool stream_out = 2 * total * 16 <= pa::kStreamWriteMax;
+  hipLaunchKernelGGL(stream_out ? pa::cache_write_kernel<true> : pa::cache_write_kernel<false>,
+                     dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(key),
                      static_cast<const uint4*>(value), static_cast<uint4*>(key_cache),
                      static_cast<uint4*>(value_cache), slot_mapping, total, Hkv * cpr, cpr, Hkv,
