@@ -355,6 +355,25 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
       narrow<DT>(dn > 0.f ? nt / dn : 0.f);
 }
 
+// The (query head, sequence) a wide-reduce workgroup combines.  With Hkv a
+// multiple of 8 the main pass writes every partial of KV head g on XCD
+// g % 8 (the hardware hands consecutive workgroups to the XCDs in turn), so
+// (s, h) goes to the workgroup that runs on XCD (h / G) % 8, where those
+// partials sit in the L2: 2 us off the long-context step.  (For the few
+// partials of reduce_kernel the grid's own order measured faster.)
+__device__ __forceinline__ void wide_reduce_item(const DecodeArgs& a, int& h, int& s) {
+  if (a.Hkv % 8) {
+    h = blockIdx.x;
+    s = blockIdx.y;
+    return;
+  }
+  const int id = blockIdx.x + gridDim.x * blockIdx.y;
+  const int x = id & 7, k = id >> 3, per = a.Hq >> 3, G = a.Hq / a.Hkv;
+  s = k / per;
+  const int j = k - s * per;
+  h = (x + 8 * (j / G)) * G + j % G;
+}
+
 // The same combination for many partitions (long contexts).  One workgroup
 // of 256 threads per (query head, sequence): a partition's row of D floats is
 // read by D/4 threads with 16-byte loads, and the 256/(D/4) thread groups
@@ -371,8 +390,8 @@ __global__ __launch_bounds__(256) void reduce_wide_kernel(DecodeArgs a) {
   constexpr int U = 4;                     // partitions per group in flight
   __shared__ float4 gnum[NG][TPR];
   __shared__ float gden[NG];
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
+  int h, s;
+  wide_reduce_item(a, h, s);
   const int t = threadIdx.x;
   const int grp = t / TPR;
   const int c = t - grp * TPR;
