@@ -358,9 +358,11 @@ __global__ __launch_bounds__(D) void reduce_kernel(DecodeArgs a) {
 // The (query head, sequence) a wide-reduce workgroup combines.  With Hkv a
 // multiple of 8 the main pass writes every partial of KV head g on XCD
 // g % 8 (the hardware hands consecutive workgroups to the XCDs in turn), so
-// (s, h) goes to the workgroup that runs on XCD (h / G) % 8, where those
-// partials sit in the L2: 2 us off the long-context step.  (For the few
-// partials of reduce_kernel the grid's own order measured faster.)
+// (s, h) goes to the workgroup that runs on XCD (h / G) % 8, the one that
+// wrote its partials.  On the long-context batch that took 2 us off the
+// step, with the same bytes fetched from memory (the partials are not L2
+// hits; the gain is in the placement's timing, not in traffic).  For the few
+// partials of reduce_kernel the grid's own order measured faster.
 __device__ __forceinline__ void wide_reduce_item(const DecodeArgs& a, int& h, int& s) {
   if (a.Hkv % 8) {
     h = blockIdx.x;
