@@ -353,6 +353,36 @@ def test_cache_write_prefill(dtype, D, bs):
     assert np.array_equal(synth.to_numpy_storage(vc), ref_v)
 
 
+def test_cache_write_both_store_policies():
+    """The cache write streams its stores out when the rows fit in 32 MiB and
+    uses the default policy above that: one call over 34 MB of rows and the
+    same rows as two calls of 17 MB leave bit-identical pools, equal to the
+    oracle's cache write (some slots -1)."""
+    NB, Hkv, bs, D, T = 1200, 40, 16, 128, 1700    # 2 * T * Hkv * D * 2 B = 34.8 MB
+    rng = np.random.default_rng(11)
+    slots = rng.permutation(NB * bs)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.05] = -1
+    g = torch.Generator(device=DEV).manual_seed(13)
+    kc0 = torch.randn(NB, Hkv, bs, D, generator=g, device=DEV).to(torch.bfloat16)
+    vc0 = torch.randn(NB, Hkv, bs, D, generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn(T, Hkv, D, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(T, Hkv, D, generator=g, device=DEV).to(torch.bfloat16)
+    s_d = torch.from_numpy(slots).to(DEV)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    pa.pa_reshape_and_cache(k, v, kc1, vc1, s_d)                     # one call, default stores
+    kc2, vc2 = kc0.clone(), vc0.clone()
+    h = T // 2
+    pa.pa_reshape_and_cache(k[:h].contiguous(), v[:h].contiguous(), kc2, vc2, s_d[:h].contiguous())
+    pa.pa_reshape_and_cache(k[h:].contiguous(), v[h:].contiguous(), kc2, vc2, s_d[h:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(bits(kc1), bits(kc2)) and torch.equal(bits(vc1), bits(vc2))
+    ref_k, ref_v = od.reshape_and_cache(synth.to_numpy_storage(k), synth.to_numpy_storage(v),
+                                        synth.to_numpy_storage(kc0), synth.to_numpy_storage(vc0),
+                                        slots)
+    assert np.array_equal(synth.to_numpy_storage(kc1), ref_k)
+    assert np.array_equal(synth.to_numpy_storage(vc1), ref_v)
+
+
 def test_copy_blocks_layers():
     L, NB, Hkv, bs, D = 20, 64, 4, 16, 128        # 20 layers: two launches of layers
     g = torch.Generator(device=DEV).manual_seed(9)
